@@ -1,0 +1,210 @@
+/*
+ * nbx_paged.h - C ABI of the paged split-KV attention library for MI355X
+ * (gfx950).  Library: libnbx_paged.so.
+ *
+ * The operation (pages: "nbxtensor attention_wrappers.py" and "nbxtensor
+ * paged_decode_attn.py", the paged KV module description, paged_kv_append,
+ * paged_decode_attention, decode_reduce; "TensorFold PR #1219" for several
+ * query rows sharing the K/V of a KV head):
+ *
+ *   A per-layer pool per K and per V holds [num_pages, kv_heads, page_tokens,
+ *   head_dim] elements; the positions of one KV head inside one page are
+ *   consecutive rows.  Sequence b owns the pages block_table[b, 0..]; its
+ *   logical position j lives in page block_table[b, j / page_tokens] at row
+ *   j % page_tokens.  New positions are written through a slot mapping,
+ *   slot = page * page_tokens + row.  A query row of head h attends KV head
+ *   h / (q_heads / kv_heads).  The keys are cut into splits of split_size
+ *   positions; each split yields an unnormalised partial (o, m, l) with an
+ *   fp32 accumulator, and the partials are merged in ascending split order.
+ *
+ * Conventions shared by every entry point:
+ *
+ *  - Pointers named in a nbx_kv_pool and every array argument are DEVICE
+ *    pointers unless stated; structs themselves are passed by host pointer
+ *    and read during the call only.
+ *  - Strides are in elements.  The last (head_dim) dimension is contiguous.
+ *  - The caller owns and allocates every buffer.  The library allocates and
+ *    frees nothing, keeps no state between calls and is re-entrant.
+ *  - All device work is enqueued on `stream` (0 = the null stream) without
+ *    synchronising; inputs must stay alive until the stream passes the work.
+ *  - Host-side validation never reads device memory.  It returns a negative
+ *    nbx_status and enqueues nothing on failure; there is no fallback path.
+ *  - Data errors that only the device can see (a slot beyond the pool, a
+ *    block-table entry outside [0, num_pages) inside a sequence, a sequence
+ *    longer than max_pages * page_tokens) are OR-ed into *dev_err when dev_err
+ *    is non-null; the offending slot / position is skipped.
+ */
+#ifndef NBX_PAGED_H
+#define NBX_PAGED_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+typedef enum {
+    NBX_F32 = 0,      /* IEEE binary32 */
+    NBX_BF16 = 1,     /* bfloat16: the upper 16 bits of a binary32 */
+    NBX_FP8_E4M3 = 2  /* OCP E4M3FN: bias 7, no infinity, 0x7F/0xFF NaN, max 448 */
+} nbx_dtype;
+
+/* status codes (return values) */
+typedef enum {
+    NBX_OK = 0,
+    NBX_ERR_NULL_PTR = -1,      /* a required pointer is null */
+    NBX_ERR_BAD_DTYPE = -2,     /* dtype code unknown or combination not supported */
+    NBX_ERR_BAD_SHAPE = -3,     /* sizes inconsistent (e.g. q_heads % kv_heads != 0,
+                                   head_dim not in {64, 128, 256}, K/V pools differ) */
+    NBX_ERR_BAD_ALIGN = -4,     /* page_tokens % 16, split_size % 16, split_size *
+                                   n_split < the longest sequence, unit stride broken */
+    NBX_ERR_WORKSPACE = -5,     /* workspace too small */
+    NBX_ERR_UNSUPPORTED = -6,   /* valid request this build does not implement */
+    NBX_ERR_LAUNCH = -7         /* the HIP runtime refused a kernel launch */
+} nbx_status;
+
+/* device-side data error bits OR-ed into *dev_err */
+#define NBX_DEVERR_SLOT_RANGE 0x1   /* append: slot >= num_pages * page_tokens */
+#define NBX_DEVERR_PAGE_RANGE 0x2   /* read: block-table entry outside [0, num_pages) */
+#define NBX_DEVERR_SEQ_RANGE 0x4    /* read: seq_len > max_pages * page_tokens, or < 0 */
+
+/* A paged K or V pool: data[page * stride_page + head * stride_head +
+ * row * stride_token + e] for e in [0, head_dim).  `scale` multiplies every
+ * stored element when read (fp8 per-tensor dequantisation factor; 1.0 for
+ * fp32 / bf16 pools) and divides a value before it is stored by an append. */
+typedef struct {
+    void *data;             /* device pointer */
+    int32_t dtype;          /* nbx_dtype */
+    int32_t num_pages;
+    int32_t kv_heads;
+    int32_t page_tokens;    /* a multiple of 16 */
+    int32_t head_dim;       /* 64, 128 or 256 */
+    int64_t stride_page;    /* elements; stride_token >= head_dim */
+    int64_t stride_head;
+    int64_t stride_token;
+    float scale;
+} nbx_kv_pool;
+
+/*
+ * nbx_paged_kv_append - write new positions into the K and V pools through a
+ * slot mapping (nbxtensor paged_decode_attn.py, paged_kv_append_kernel;
+ * nbxtensor attention_wrappers.py, paged_kv_append).
+ *
+ *   new_k, new_v   device, [n_tok, kv_heads, head_dim] of new_dtype, element
+ *                  (t, h, e) at t * new_stride_tok + h * new_stride_head + e.
+ *                  new_v (and v_pool) may be null to write K only.
+ *   new_dtype      NBX_F32 or NBX_BF16.
+ *   slot_mapping   device int32 [n_tok]; slot = page * page_tokens + row.
+ *                  A negative slot is skipped (padding).  A slot at or beyond
+ *                  num_pages * page_tokens is skipped and sets
+ *                  NBX_DEVERR_SLOT_RANGE.  Two equal slots: unspecified winner.
+ *
+ * Stored value: same dtype -> bit copy; fp32 -> bf16 round-to-nearest-even
+ * (NaN -> 0x7FC0 with the sign kept); bf16 -> fp32 exact; to fp8:
+ * round-to-nearest-even of the fp32 quotient value / pool.scale, saturating at
+ * +-448, NaN -> 0x7F with the sign kept.  n_tok == 0 is a no-op.
+ */
+int nbx_paged_kv_append(const void *new_k, const void *new_v, int32_t new_dtype, int64_t n_tok,
+                        int64_t new_stride_tok, int64_t new_stride_head,
+                        const nbx_kv_pool *k_pool, const nbx_kv_pool *v_pool,
+                        const int32_t *slot_mapping, int32_t *dev_err, hipStream_t stream);
+
+/*
+ * nbx_paged_decode_plan - host only.  The split rule of the nbxtensor
+ * paged_decode_attn.py page (paged_decode_splits and the kernel's seg_len):
+ *   n_split    = max(1, min(ceil(longest / split_positions), max_splits))
+ *   split_size = ceil(ceil(longest / n_split) / 16) * 16
+ * with longest = max(max_seq_len, 1).  The pages use split_positions = 256
+ * and max_splits = 64.  split_positions, max_splits > 0 or NBX_ERR_BAD_SHAPE.
+ */
+int nbx_paged_decode_plan(int32_t max_seq_len, int32_t split_positions, int32_t max_splits,
+                          int32_t *n_split, int32_t *split_size);
+
+/* nbx_paged_decode_workspace_bytes - host only.  Bytes of workspace that
+ * nbx_paged_decode needs for `rows` query rows: the partials o [rows,
+ * n_split, head_dim], m and l [rows, n_split], fp32, each 256-byte aligned. */
+size_t nbx_paged_decode_workspace_bytes(int64_t rows, int32_t n_split, int32_t head_dim);
+
+/*
+ * nbx_paged_decode_partial - the split partials (nbxtensor paged_decode_attn.py,
+ * paged_decode_attn_split_kernel; several rows per KV head as in TensorFold
+ * PR #1219).
+ *
+ *   q            device, [batch, q_heads, q_rows, head_dim] contiguous, NBX_F32
+ *                or NBX_BF16 (read exactly, never rounded).  Query row index
+ *                row = (b * q_heads + h) * q_rows + r.
+ *   causal       0: every row of sequence b sees keys [0, seq_lens[b]).
+ *                1: row r sees keys [0, seq_lens[b] - q_rows + r], i.e. the
+ *                q_rows rows are the last q_rows positions of the sequence,
+ *                already in the pool.
+ *   k_pool/v_pool  same dtype, num_pages, kv_heads, page_tokens, head_dim.
+ *   block_table  device int32 [batch, max_pages] (row stride max_pages), -1
+ *                past each sequence.  Entries covering [0, seq_lens[b]) must
+ *                lie in [0, num_pages); a violation sets NBX_DEVERR_PAGE_RANGE
+ *                and that page's positions are skipped.
+ *   seq_lens     device int32 [batch]; positions held by each sequence.
+ *   scale        softmax scale applied to q . k (after pool.scale).
+ *   split_size   positions per split, a multiple of 16; split s covers
+ *                [s * split_size, min((s + 1) * split_size, n)) of the keys a
+ *                row sees.  split_size * n_split must cover every sequence
+ *                (not checkable on the host: longer sequences set
+ *                NBX_DEVERR_SEQ_RANGE and their tail is not read).
+ *   o_part       device fp32 [rows, n_split, head_dim]: sum_j exp(s_j - m) v_j
+ *   m_part       device fp32 [rows, n_split]: max_j s_j (natural-log units)
+ *   l_part       device fp32 [rows, n_split]: sum_j exp(s_j - m)
+ *                where s_j = scale * pool.scale_k * (q . k_j) over the split.
+ *                An empty split stores (0, -inf, 0).
+ *
+ * Supported: pool dtype NBX_F32 with any q dtype; NBX_BF16 or NBX_FP8_E4M3
+ * pools with NBX_BF16 or NBX_F32 q.
+ */
+int nbx_paged_decode_partial(const void *q, int32_t q_dtype, int32_t batch, int32_t q_heads,
+                             int32_t q_rows, int32_t causal, const nbx_kv_pool *k_pool,
+                             const nbx_kv_pool *v_pool, const int32_t *block_table,
+                             int32_t max_pages, const int32_t *seq_lens, float scale,
+                             int32_t split_size, int32_t n_split, float *o_part, float *m_part,
+                             float *l_part, int32_t *dev_err, hipStream_t stream);
+
+/*
+ * nbx_paged_decode_merge - fixed-order combine of split partials (nbxtensor
+ * attention_wrappers.py, decode_reduce): per row, M = the largest m_s of the
+ * non-empty splits (m_s != -inf), w_s = exp(m_s - M), and
+ *   out = sum_s w_s o_s / sum_s w_s l_s,
+ * summed in ascending s.  A row with no non-empty split is 0.  NaN in a
+ * partial propagates to the row.
+ *
+ *   o_part, m_part, l_part  as written by nbx_paged_decode_partial.
+ *   out          device [rows, head_dim] of out_dtype (NBX_F32 or NBX_BF16,
+ *                bf16 rounded to nearest even).
+ */
+int nbx_paged_decode_merge(const float *o_part, const float *m_part, const float *l_part,
+                           int64_t rows, int32_t n_split, int32_t head_dim, void *out,
+                           int32_t out_dtype, hipStream_t stream);
+
+/*
+ * nbx_paged_decode - partial then merge on one stream (nbxtensor
+ * attention_wrappers.py, paged_decode_attention).  Arguments as for the two
+ * calls; `workspace` (device, at least nbx_paged_decode_workspace_bytes(rows,
+ * n_split, head_dim) bytes, 256-byte aligned) holds the partials.
+ */
+int nbx_paged_decode(const void *q, int32_t q_dtype, int32_t batch, int32_t q_heads,
+                     int32_t q_rows, int32_t causal, const nbx_kv_pool *k_pool,
+                     const nbx_kv_pool *v_pool, const int32_t *block_table, int32_t max_pages,
+                     const int32_t *seq_lens, float scale, int32_t split_size, int32_t n_split,
+                     void *workspace, size_t workspace_bytes, void *out, int32_t out_dtype,
+                     int32_t *dev_err, hipStream_t stream);
+
+/* nbx_status_str - static message text for a status code (never null). */
+const char *nbx_status_str(int status);
+
+/* nbx_version - library version as major * 10000 + minor * 100 + patch. */
+int nbx_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NBX_PAGED_H */

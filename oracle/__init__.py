@@ -63,6 +63,7 @@ def _load():
             lib.oracle_merge.argtypes = [P, P, P, I64, I, I, P]
             lib.oracle_set_mutation.argtypes = [I]
             lib.oracle_get_mutation.restype = I
+            lib.oracle_num_threads.restype = I
             _lib = lib
     return _lib
 
@@ -96,6 +97,11 @@ class mutation:
 
     def __exit__(self, *exc):
         _load().oracle_set_mutation(0)
+
+
+def num_threads() -> int:
+    """Threads the oracle's parallel loops run on."""
+    return int(_load().oracle_num_threads())
 
 
 def decode_values(dtype: str, raw) -> np.ndarray:

@@ -47,6 +47,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <omp.h>
+
 enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_E4M3 = 2 };
 
 /* planted mistakes, used only by the checker-sanity tests */
@@ -519,3 +521,15 @@ void oracle_merge(const double *o, const double *m, const double *l, int64_t row
 }
 
 size_t oracle_elem_size(int dtype) { return elem_size(dtype); }
+
+/* threads the OpenMP loops above use */
+int oracle_num_threads(void)
+{
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        n = omp_get_num_threads();
+    }
+    return n;
+}

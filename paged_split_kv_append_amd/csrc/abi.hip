@@ -1,0 +1,307 @@
+// C-ABI entry points of libnbx_paged: host validation, the split plan, the
+// workspace layout and kernel dispatch.  Nothing here reads device memory or
+// allocates; every launch goes to the caller's stream.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kernels.h"
+#include "nbx_paged.h"
+
+namespace {
+
+constexpr int kMaxGridYZ = 65535;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool dtype_ok(int32_t d) { return d == NBX_F32 || d == NBX_BF16 || d == NBX_FP8_E4M3; }
+
+bool head_dim_ok(int32_t d) { return d == 64 || d == 128 || d == 256; }
+
+// geometry and alignment of one pool; returns NBX_OK or an error
+int check_pool(const nbx_kv_pool *p)
+{
+    if (!p || !p->data)
+        return NBX_ERR_NULL_PTR;
+    if (!dtype_ok(p->dtype))
+        return NBX_ERR_BAD_DTYPE;
+    if (p->num_pages < 1 || p->kv_heads < 1 || !head_dim_ok(p->head_dim))
+        return NBX_ERR_BAD_SHAPE;
+    if (p->page_tokens < 16 || p->page_tokens % 16)
+        return NBX_ERR_BAD_ALIGN;
+    if (p->stride_token < p->head_dim || p->stride_head < 0 || p->stride_page < 0)
+        return NBX_ERR_BAD_SHAPE;
+    // 16-element strides and 16-byte base: every K/V row starts 16-byte aligned
+    if (p->stride_token % 16 || p->stride_head % 16 || p->stride_page % 16 || !aligned16(p->data))
+        return NBX_ERR_BAD_ALIGN;
+    if (!(p->scale > 0.0f) || p->scale == INFINITY)
+        return NBX_ERR_BAD_SHAPE;
+    return NBX_OK;
+}
+
+bool same_geometry(const nbx_kv_pool *a, const nbx_kv_pool *b)
+{
+    return a->dtype == b->dtype && a->num_pages == b->num_pages && a->kv_heads == b->kv_heads &&
+           a->page_tokens == b->page_tokens && a->head_dim == b->head_dim;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int to_status(hipError_t e) { return e == hipSuccess ? NBX_OK : NBX_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int nbx_version(void) { return 100; }
+
+const char *nbx_status_str(int status)
+{
+    switch (status) {
+    case NBX_OK: return "ok";
+    case NBX_ERR_NULL_PTR: return "a required pointer is null";
+    case NBX_ERR_BAD_DTYPE: return "unknown or unsupported element type";
+    case NBX_ERR_BAD_SHAPE: return "inconsistent sizes";
+    case NBX_ERR_BAD_ALIGN: return "alignment: page_tokens / split_size not a multiple of 16, "
+                                   "strides not multiples of 16 elements, or a pointer not "
+                                   "16-byte aligned";
+    case NBX_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case NBX_ERR_UNSUPPORTED: return "request not supported by this build";
+    case NBX_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int nbx_paged_decode_plan(int32_t max_seq_len, int32_t split_positions, int32_t max_splits,
+                          int32_t *n_split, int32_t *split_size)
+{
+    if (!n_split || !split_size)
+        return NBX_ERR_NULL_PTR;
+    if (split_positions <= 0 || max_splits <= 0)
+        return NBX_ERR_BAD_SHAPE;
+    const int64_t longest = max_seq_len < 1 ? 1 : max_seq_len;
+    int64_t n = (longest + split_positions - 1) / split_positions;
+    if (n > max_splits)
+        n = max_splits;
+    if (n < 1)
+        n = 1;
+    const int64_t per = (longest + n - 1) / n;
+    *n_split = (int32_t)n;
+    *split_size = (int32_t)((per + 15) / 16 * 16);
+    return NBX_OK;
+}
+
+size_t nbx_paged_decode_workspace_bytes(int64_t rows, int32_t n_split, int32_t head_dim)
+{
+    if (rows <= 0 || n_split <= 0 || head_dim <= 0)
+        return 0;
+    const size_t o = (size_t)rows * n_split * head_dim * sizeof(float);
+    const size_t ml = (size_t)rows * n_split * sizeof(float);
+    return round256(o) + 2 * round256(ml);
+}
+
+int nbx_paged_kv_append(const void *new_k, const void *new_v, int32_t new_dtype, int64_t n_tok,
+                        int64_t new_stride_tok, int64_t new_stride_head,
+                        const nbx_kv_pool *k_pool, const nbx_kv_pool *v_pool,
+                        const int32_t *slot_mapping, int32_t *dev_err, hipStream_t stream)
+{
+    if (!new_k || !k_pool || !slot_mapping)
+        return NBX_ERR_NULL_PTR;
+    if ((new_v == nullptr) != (v_pool == nullptr))
+        return NBX_ERR_NULL_PTR;
+    if (new_dtype != NBX_F32 && new_dtype != NBX_BF16)
+        return NBX_ERR_BAD_DTYPE;
+    int st = check_pool(k_pool);
+    if (st != NBX_OK)
+        return st;
+    if (v_pool) {
+        if ((st = check_pool(v_pool)) != NBX_OK)
+            return st;
+        if (!same_geometry(k_pool, v_pool))
+            return NBX_ERR_BAD_SHAPE;
+    }
+    if (n_tok < 0 || new_stride_head < k_pool->head_dim || new_stride_tok < 0)
+        return NBX_ERR_BAD_SHAPE;
+    if (new_stride_tok % 8 || new_stride_head % 8 || !aligned16(new_k) ||
+        (new_v && !aligned16(new_v)))
+        return NBX_ERR_BAD_ALIGN;
+    if (n_tok == 0)
+        return NBX_OK;
+    if (n_tok * k_pool->kv_heads * (k_pool->head_dim / 8) > (int64_t)INT32_MAX * 256)
+        return NBX_ERR_BAD_SHAPE;
+
+    nbx::AppendArgs a{};
+    a.new_k = new_k;
+    a.new_v = new_v;
+    a.src_dtype = new_dtype;
+    a.dst_dtype = k_pool->dtype;
+    a.n_tok = n_tok;
+    a.new_stride_tok = new_stride_tok;
+    a.new_stride_head = new_stride_head;
+    a.kv_heads = k_pool->kv_heads;
+    a.head_dim = k_pool->head_dim;
+    a.num_pages = k_pool->num_pages;
+    a.page_tokens = k_pool->page_tokens;
+    a.k_data = k_pool->data;
+    a.k_stride_page = k_pool->stride_page;
+    a.k_stride_head = k_pool->stride_head;
+    a.k_stride_token = k_pool->stride_token;
+    a.k_scale = k_pool->scale;
+    if (v_pool) {
+        a.v_data = v_pool->data;
+        a.v_stride_page = v_pool->stride_page;
+        a.v_stride_head = v_pool->stride_head;
+        a.v_stride_token = v_pool->stride_token;
+        a.v_scale = v_pool->scale;
+    }
+    a.slot_mapping = slot_mapping;
+    a.dev_err = dev_err;
+    return to_status(nbx::launch_append(a, stream));
+}
+
+static int validate_partial(const void *q, int32_t q_dtype, int32_t batch, int32_t q_heads,
+                            int32_t q_rows, int32_t causal, const nbx_kv_pool *k_pool,
+                            const nbx_kv_pool *v_pool, const int32_t *block_table,
+                            int32_t max_pages, const int32_t *seq_lens, float scale,
+                            int32_t split_size, int32_t n_split)
+{
+    if (!q || !k_pool || !v_pool || !block_table || !seq_lens)
+        return NBX_ERR_NULL_PTR;
+    if (q_dtype != NBX_F32 && q_dtype != NBX_BF16)
+        return NBX_ERR_BAD_DTYPE;
+    int st = check_pool(k_pool);
+    if (st != NBX_OK)
+        return st;
+    if ((st = check_pool(v_pool)) != NBX_OK)
+        return st;
+    if (!same_geometry(k_pool, v_pool))
+        return NBX_ERR_BAD_SHAPE;
+    if (batch < 0 || q_heads < 1 || q_rows < 1 || max_pages < 1 || (causal != 0 && causal != 1))
+        return NBX_ERR_BAD_SHAPE;
+    if (q_heads % k_pool->kv_heads)
+        return NBX_ERR_BAD_SHAPE;
+    if (scale != scale || scale == INFINITY || scale == -INFINITY)
+        return NBX_ERR_BAD_SHAPE;
+    if (split_size < 16 || split_size % 16)
+        return NBX_ERR_BAD_ALIGN;
+    if (n_split < 1 || n_split > kMaxGridYZ)
+        return NBX_ERR_BAD_SHAPE;
+    if ((int64_t)batch * k_pool->kv_heads > kMaxGridYZ)
+        return NBX_ERR_UNSUPPORTED;
+    if ((int64_t)split_size * n_split > INT32_MAX || (int64_t)max_pages * k_pool->page_tokens > INT32_MAX)
+        return NBX_ERR_BAD_SHAPE;
+    if (!aligned16(q))
+        return NBX_ERR_BAD_ALIGN;
+    return NBX_OK;
+}
+
+int nbx_paged_decode_partial(const void *q, int32_t q_dtype, int32_t batch, int32_t q_heads,
+                             int32_t q_rows, int32_t causal, const nbx_kv_pool *k_pool,
+                             const nbx_kv_pool *v_pool, const int32_t *block_table,
+                             int32_t max_pages, const int32_t *seq_lens, float scale,
+                             int32_t split_size, int32_t n_split, float *o_part, float *m_part,
+                             float *l_part, int32_t *dev_err, hipStream_t stream)
+{
+    int st = validate_partial(q, q_dtype, batch, q_heads, q_rows, causal, k_pool, v_pool,
+                              block_table, max_pages, seq_lens, scale, split_size, n_split);
+    if (st != NBX_OK)
+        return st;
+    if (!o_part || !m_part || !l_part)
+        return NBX_ERR_NULL_PTR;
+    if (!aligned16(o_part) || ((uintptr_t)m_part & 3u) || ((uintptr_t)l_part & 3u))
+        return NBX_ERR_BAD_ALIGN;
+    if (batch == 0)
+        return NBX_OK;
+
+    nbx::PartialArgs a{};
+    a.q = q;
+    a.q_dtype = q_dtype;
+    a.kv_dtype = k_pool->dtype;
+    a.batch = batch;
+    a.q_heads = q_heads;
+    a.q_rows = q_rows;
+    a.causal = causal;
+    a.kv_heads = k_pool->kv_heads;
+    a.group = q_heads / k_pool->kv_heads;
+    a.rows_per_kv = a.group * q_rows;
+    a.head_dim = k_pool->head_dim;
+    a.num_pages = k_pool->num_pages;
+    a.page_tokens = k_pool->page_tokens;
+    a.k_data = k_pool->data;
+    a.k_stride_page = k_pool->stride_page;
+    a.k_stride_head = k_pool->stride_head;
+    a.k_stride_token = k_pool->stride_token;
+    a.v_data = v_pool->data;
+    a.v_stride_page = v_pool->stride_page;
+    a.v_stride_head = v_pool->stride_head;
+    a.v_stride_token = v_pool->stride_token;
+    a.k_scale = k_pool->scale;
+    a.v_scale = v_pool->scale;
+    a.block_table = block_table;
+    a.max_pages = max_pages;
+    a.seq_lens = seq_lens;
+    a.scale = scale;
+    a.split_size = split_size;
+    a.n_split = n_split;
+    a.o_part = o_part;
+    a.m_part = m_part;
+    a.l_part = l_part;
+    a.dev_err = dev_err;
+    return to_status(nbx::launch_partial_valu(a, stream));
+}
+
+int nbx_paged_decode_merge(const float *o_part, const float *m_part, const float *l_part,
+                           int64_t rows, int32_t n_split, int32_t head_dim, void *out,
+                           int32_t out_dtype, hipStream_t stream)
+{
+    if (!o_part || !m_part || !l_part || !out)
+        return NBX_ERR_NULL_PTR;
+    if (out_dtype != NBX_F32 && out_dtype != NBX_BF16)
+        return NBX_ERR_BAD_DTYPE;
+    if (rows < 0 || n_split < 1 || !head_dim_ok(head_dim))
+        return NBX_ERR_BAD_SHAPE;
+    if (!aligned16(o_part) || !aligned16(out) || ((uintptr_t)m_part & 3u) ||
+        ((uintptr_t)l_part & 3u))
+        return NBX_ERR_BAD_ALIGN;
+    if ((rows + 3) / 4 > INT32_MAX)
+        return NBX_ERR_BAD_SHAPE;
+    nbx::MergeArgs a{o_part, m_part, l_part, rows, n_split, head_dim, out, out_dtype};
+    return to_status(nbx::launch_merge(a, stream));
+}
+
+int nbx_paged_decode(const void *q, int32_t q_dtype, int32_t batch, int32_t q_heads,
+                     int32_t q_rows, int32_t causal, const nbx_kv_pool *k_pool,
+                     const nbx_kv_pool *v_pool, const int32_t *block_table, int32_t max_pages,
+                     const int32_t *seq_lens, float scale, int32_t split_size, int32_t n_split,
+                     void *workspace, size_t workspace_bytes, void *out, int32_t out_dtype,
+                     int32_t *dev_err, hipStream_t stream)
+{
+    int st = validate_partial(q, q_dtype, batch, q_heads, q_rows, causal, k_pool, v_pool,
+                              block_table, max_pages, seq_lens, scale, split_size, n_split);
+    if (st != NBX_OK)
+        return st;
+    if (!out)
+        return NBX_ERR_NULL_PTR;
+    if (out_dtype != NBX_F32 && out_dtype != NBX_BF16)
+        return NBX_ERR_BAD_DTYPE;
+    if (batch == 0)
+        return NBX_OK;
+    const int64_t rows = (int64_t)batch * q_heads * q_rows;
+    const int32_t D = k_pool->head_dim;
+    const size_t need = nbx_paged_decode_workspace_bytes(rows, n_split, D);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
+        return NBX_ERR_WORKSPACE;
+    char *ws = (char *)workspace;
+    float *o_part = (float *)ws;
+    float *m_part = (float *)(ws + round256((size_t)rows * n_split * D * sizeof(float)));
+    float *l_part = (float *)((char *)m_part + round256((size_t)rows * n_split * sizeof(float)));
+    st = nbx_paged_decode_partial(q, q_dtype, batch, q_heads, q_rows, causal, k_pool, v_pool,
+                                  block_table, max_pages, seq_lens, scale, split_size, n_split,
+                                  o_part, m_part, l_part, dev_err, stream);
+    if (st != NBX_OK)
+        return st;
+    return nbx_paged_decode_merge(o_part, m_part, l_part, rows, n_split, D, out, out_dtype,
+                                  stream);
+}
+
+}  // extern "C"

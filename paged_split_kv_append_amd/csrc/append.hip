@@ -1,0 +1,123 @@
+// Paged KV append: new positions written into the K and V pools through the
+// slot mapping (nbxtensor paged_decode_attn.py, paged_kv_append_kernel: one
+// slot per new token, slot = page * page_tokens + row, the values cast to the
+// pool's dtype on store).
+//
+// One thread moves 8 consecutive elements of one (token, KV head) row, so a
+// row of D elements takes D/8 threads and the K and V pools are written by
+// the same launch (blockIdx.y selects K or V).
+#include "device_common.h"
+#include "kernels.h"
+
+namespace nbx {
+
+template <int SRC>
+__device__ __forceinline__ void load8(const void *src, int64_t i, float (&x)[8])
+{
+    if constexpr (SRC == NBX_F32) {
+        const float4 *p = (const float4 *)((const float *)src + i);
+        float4 a = p[0], b = p[1];
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    } else {
+        uint4 w = *(const uint4 *)((const uint16_t *)src + i);
+        uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            x[2 * k] = __uint_as_float(ws[k] << 16);
+            x[2 * k + 1] = __uint_as_float(ws[k] & 0xFFFF0000u);
+        }
+    }
+}
+
+template <int SRC, int DST>
+__device__ __forceinline__ void store8(void *dst, int64_t i, const float (&x)[8], float inv_scale_div,
+                                       const void *src, int64_t si)
+{
+    if constexpr (DST == NBX_F32) {
+        float4 *p = (float4 *)((float *)dst + i);
+        p[0] = make_float4(x[0], x[1], x[2], x[3]);
+        p[1] = make_float4(x[4], x[5], x[6], x[7]);
+    } else if constexpr (DST == NBX_BF16) {
+        if constexpr (SRC == NBX_BF16) {
+            // same dtype: bit copy
+            *(uint4 *)((uint16_t *)dst + i) = *(const uint4 *)((const uint16_t *)src + si);
+        } else {
+            uint32_t w[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                w[k] = (uint32_t)f32_to_bf16_bits(x[2 * k]) |
+                       ((uint32_t)f32_to_bf16_bits(x[2 * k + 1]) << 16);
+            *(uint4 *)((uint16_t *)dst + i) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    } else {
+        // fp8: code of the correctly rounded fp32 quotient x / scale
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            lo |= (uint32_t)f32_to_e4m3(__fdiv_rn(x[k], inv_scale_div)) << (8 * k);
+            hi |= (uint32_t)f32_to_e4m3(__fdiv_rn(x[k + 4], inv_scale_div)) << (8 * k);
+        }
+        *(uint2 *)((uint8_t *)dst + i) = make_uint2(lo, hi);
+    }
+}
+
+template <int SRC, int DST>
+__global__ void __launch_bounds__(256)
+paged_append_kernel(AppendArgs a)
+{
+    const int64_t chunks_per_row = a.head_dim / 8;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t total = a.n_tok * a.kv_heads * chunks_per_row;
+    if (gid >= total)
+        return;
+    const bool is_v = blockIdx.y == 1;
+    const void *src = is_v ? a.new_v : a.new_k;
+    void *pool = is_v ? a.v_data : a.k_data;
+    const int64_t sp = is_v ? a.v_stride_page : a.k_stride_page;
+    const int64_t sh = is_v ? a.v_stride_head : a.k_stride_head;
+    const int64_t st = is_v ? a.v_stride_token : a.k_stride_token;
+    const float scale = is_v ? a.v_scale : a.k_scale;
+
+    const int64_t c = gid % chunks_per_row;
+    const int64_t h = (gid / chunks_per_row) % a.kv_heads;
+    const int64_t t = gid / (chunks_per_row * a.kv_heads);
+    const int64_t slot = a.slot_mapping[t];
+    if (slot < 0)
+        return;                                            // padding token
+    if (slot >= (int64_t)a.num_pages * a.page_tokens) {
+        if (c == 0 && h == 0 && !is_v)
+            flag_error(a.dev_err, NBX_DEVERR_SLOT_RANGE);
+        return;
+    }
+    const int64_t page = slot / a.page_tokens;
+    const int64_t row = slot - page * a.page_tokens;
+    const int64_t si = t * a.new_stride_tok + h * a.new_stride_head + c * 8;
+    const int64_t di = page * sp + h * sh + row * st + c * 8;
+    float x[8];
+    load8<SRC>(src, si, x);
+    store8<SRC, DST>(pool, di, x, scale, src, si);
+}
+
+template <int SRC, int DST>
+static hipError_t launch_append_t(const AppendArgs &a, hipStream_t stream)
+{
+    const int64_t total = a.n_tok * a.kv_heads * (a.head_dim / 8);
+    dim3 grid((unsigned)((total + 255) / 256), a.new_v ? 2 : 1);
+    hipLaunchKernelGGL((paged_append_kernel<SRC, DST>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_append(const AppendArgs &a, hipStream_t stream)
+{
+    if (a.src_dtype == NBX_F32) {
+        if (a.dst_dtype == NBX_F32) return launch_append_t<NBX_F32, NBX_F32>(a, stream);
+        if (a.dst_dtype == NBX_BF16) return launch_append_t<NBX_F32, NBX_BF16>(a, stream);
+        return launch_append_t<NBX_F32, NBX_FP8_E4M3>(a, stream);
+    }
+    if (a.dst_dtype == NBX_F32) return launch_append_t<NBX_BF16, NBX_F32>(a, stream);
+    if (a.dst_dtype == NBX_BF16) return launch_append_t<NBX_BF16, NBX_BF16>(a, stream);
+    return launch_append_t<NBX_BF16, NBX_FP8_E4M3>(a, stream);
+}
+
+}  // namespace nbx

@@ -1,0 +1,59 @@
+// Internal launch interface between the C-ABI entry points and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "nbx_paged.h"
+
+namespace nbx {
+
+struct AppendArgs {
+    const void *new_k;
+    const void *new_v;          // null: K only
+    int32_t src_dtype, dst_dtype;
+    int64_t n_tok, new_stride_tok, new_stride_head;
+    int32_t kv_heads, head_dim, num_pages, page_tokens;
+    void *k_data;
+    int64_t k_stride_page, k_stride_head, k_stride_token;
+    void *v_data;
+    int64_t v_stride_page, v_stride_head, v_stride_token;
+    float k_scale, v_scale;
+    const int32_t *slot_mapping;
+    int32_t *dev_err;
+};
+
+struct PartialArgs {
+    const void *q;
+    int32_t q_dtype, kv_dtype;
+    int32_t batch, q_heads, q_rows, causal;
+    int32_t kv_heads, group;        // group = q_heads / kv_heads
+    int32_t rows_per_kv;            // group * q_rows: rows sharing one KV head
+    int32_t head_dim, num_pages, page_tokens;
+    const void *k_data;
+    int64_t k_stride_page, k_stride_head, k_stride_token;
+    const void *v_data;
+    int64_t v_stride_page, v_stride_head, v_stride_token;
+    float k_scale, v_scale;
+    const int32_t *block_table;
+    int32_t max_pages;
+    const int32_t *seq_lens;
+    float scale;                    // softmax scale
+    int32_t split_size, n_split;
+    float *o_part, *m_part, *l_part;
+    int32_t *dev_err;
+};
+
+struct MergeArgs {
+    const float *o_part, *m_part, *l_part;
+    int64_t rows;
+    int32_t n_split, head_dim;
+    void *out;
+    int32_t out_dtype;
+};
+
+hipError_t launch_append(const AppendArgs &a, hipStream_t stream);
+hipError_t launch_partial_valu(const PartialArgs &a, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs &a, hipStream_t stream);
+
+}  // namespace nbx

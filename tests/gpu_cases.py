@@ -1,0 +1,76 @@
+"""Helpers for the GPU tests: move a synthetic case to the device and run the
+library on it through the C ABI (via the ctypes binding)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from paged_split_kv_append_amd import binding as nb
+from paged_split_kv_append_amd import synth
+
+TOL = {"f32": 1e-5, "bf16": 2e-3, "fp8": 2e-2}
+
+
+class DevCase:
+    def __init__(self, case: synth.PagedCase, device="cuda"):
+        self.case = case
+        self.q = case.q.to(device)
+        self.k = case.k_pool.to(device)
+        self.v = case.v_pool.to(device)
+        self.bt = torch.from_numpy(case.block_table).to(device)
+        self.lens = torch.from_numpy(case.seq_lens).to(device)
+        self.new_k = case.new_k.to(device) if case.new_k is not None else None
+        self.new_v = case.new_v.to(device) if case.new_v is not None else None
+        self.slots = (torch.from_numpy(case.slot_mapping).to(device)
+                      if case.slot_mapping is not None else None)
+        self.err = torch.zeros(1, dtype=torch.int32, device=device)
+
+    def pools(self):
+        return nb.KVPool(self.k, self.case.k_scale), nb.KVPool(self.v, self.case.v_scale)
+
+    def plan(self):
+        pol = self.case.split_policy
+        if pol[0] == "fixed":
+            return pol[2], pol[1]
+        n, s = nb.nbx_paged_decode_plan(int(self.case.seq_lens.max()), pol[1], pol[2])
+        return n, s
+
+    def append(self):
+        kp, vp = self.pools()
+        nb.nbx_paged_kv_append(self.new_k, self.new_v, kp, vp, self.slots, dev_err=self.err)
+
+    def decode(self, n_split=None, split_size=None, out_dtype=torch.float32):
+        if n_split is None:
+            n_split, split_size = self.plan()
+        c = self.case
+        kp, vp = self.pools()
+        rows = c.rows
+        ws = torch.empty(nb.nbx_paged_decode_workspace_bytes(rows, n_split, c.head_dim),
+                         dtype=torch.uint8, device=self.q.device)
+        out = torch.empty(c.batch, c.q_heads, c.q_rows, c.head_dim, dtype=out_dtype,
+                          device=self.q.device)
+        nb.nbx_paged_decode(self.q, kp, vp, self.bt, self.lens, c.softmax_scale, split_size,
+                            n_split, ws, out, causal=c.causal, dev_err=self.err)
+        return out.reshape(rows, c.head_dim)
+
+    def partial(self, n_split=None, split_size=None):
+        if n_split is None:
+            n_split, split_size = self.plan()
+        c = self.case
+        kp, vp = self.pools()
+        dev = self.q.device
+        o = torch.empty(c.rows, n_split, c.head_dim, dtype=torch.float32, device=dev)
+        m = torch.empty(c.rows, n_split, dtype=torch.float32, device=dev)
+        l = torch.empty(c.rows, n_split, dtype=torch.float32, device=dev)
+        nb.nbx_paged_decode_partial(self.q, kp, vp, self.bt, self.lens, c.softmax_scale,
+                                    split_size, n_split, o, m, l, causal=c.causal,
+                                    dev_err=self.err)
+        return o, m, l
+
+    def err_bits(self) -> int:
+        return int(self.err.item())
+
+
+def max_abs(gpu: torch.Tensor, ref: np.ndarray) -> float:
+    g = gpu.detach().double().cpu().numpy().reshape(ref.shape)
+    return float(np.max(np.abs(g - ref))) if ref.size else 0.0

@@ -1,0 +1,135 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+symbol, its host-only functions agree with the oracle, and host validation
+refuses bad requests with the documented status before touching the device."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+from paged_split_kv_append_amd import binding as nb
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return nb.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = nb.declared_symbols()
+    assert {"nbx_paged_kv_append", "nbx_paged_decode_partial", "nbx_paged_decode_merge",
+            "nbx_paged_decode", "nbx_paged_decode_plan", "nbx_paged_decode_workspace_bytes",
+            "nbx_status_str", "nbx_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for st in range(0, -8, -1):
+        s = nb.status_str(st)
+        assert s and s != "unknown status"
+    assert nb.status_str(-99) == "unknown status"
+
+
+def test_split_plan_matches_oracle_bit_exact():
+    for L in list(range(0, 5000, 7)) + [16383, 16384, 16385, 32768, 100000, 131072, 2 ** 31 - 1]:
+        for pos, cap in ((256, 64), (2048, 16), (16, 1024)):
+            assert nb.nbx_paged_decode_plan(L, pos, cap) == oracle.split_plan(max(L, 1), pos, cap)
+
+
+def test_plan_rejects_bad_arguments(lib):
+    n = ctypes.c_int32()
+    s = ctypes.c_int32()
+    assert lib.nbx_paged_decode_plan(100, 0, 64, ctypes.byref(n), ctypes.byref(s)) == -3
+    assert lib.nbx_paged_decode_plan(100, 256, 0, ctypes.byref(n), ctypes.byref(s)) == -3
+    assert lib.nbx_paged_decode_plan(100, 256, 64, None, ctypes.byref(s)) == -1
+
+
+def test_workspace_bytes():
+    assert nb.nbx_paged_decode_workspace_bytes(0, 4, 128) == 0
+    rows, ns, D = 1000, 17, 128
+    got = nb.nbx_paged_decode_workspace_bytes(rows, ns, D)
+    r = lambda x: (x + 255) // 256 * 256
+    assert got == r(rows * ns * D * 4) + 2 * r(rows * ns * 4)
+
+
+# -------------------------------------------------------------- host validation
+
+FAKE = 1 << 20          # a 16-byte aligned non-null address; validation must fail first
+
+
+def pool(**kw):
+    d = dict(data=FAKE, dtype=1, num_pages=8, kv_heads=2, page_tokens=16, head_dim=128,
+             stride_page=2 * 16 * 128, stride_head=16 * 128, stride_token=128, scale=1.0)
+    d.update(kw)
+    return nb.nbx_kv_pool(**d)
+
+
+def partial_status(lib, k=None, v=None, q_dtype=1, batch=2, q_heads=4, q_rows=1, causal=0,
+                   max_pages=4, split=256, n_split=2, q=FAKE, bt=FAKE, sl=FAKE, o=FAKE, m=FAKE,
+                   l=FAKE, scale=0.1):
+    k = k or pool()
+    v = v or pool()
+    return lib.nbx_paged_decode_partial(q, q_dtype, batch, q_heads, q_rows, causal,
+                                        ctypes.byref(k), ctypes.byref(v), bt, max_pages, sl,
+                                        scale, split, n_split, o, m, l, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(bt=None), -1), (dict(sl=None), -1), (dict(o=None), -1),
+    (dict(q_dtype=2), -2), (dict(q_dtype=7), -2),
+    (dict(k=pool(dtype=5)), -2),
+    (dict(k=pool(head_dim=96, stride_token=96)), -3),
+    (dict(q_heads=3), -3),
+    (dict(k=pool(kv_heads=4)), -3),
+    (dict(k=pool(page_tokens=8)), -4), (dict(k=pool(page_tokens=24)), -4),
+    (dict(split=100), -4), (dict(split=0), -4),
+    (dict(n_split=0), -3),
+    (dict(k=pool(stride_token=136)), -4),
+    (dict(k=pool(data=FAKE + 8)), -4),
+    (dict(q=FAKE + 4), -4),
+    (dict(k=pool(scale=0.0)), -3),
+    (dict(scale=float("nan")), -3),
+    (dict(causal=2), -3), (dict(q_rows=0), -3), (dict(max_pages=0), -3),
+    (dict(k=pool(dtype=0), v=pool(dtype=1)), -3),
+    (dict(batch=0), 0),
+])
+def test_partial_validation(lib, kw, status):
+    assert partial_status(lib, **kw) == status
+
+
+def test_append_validation(lib):
+    k, v = pool(), pool()
+    f = lambda nk=FAKE, nv=FAKE, dt=0, n=4, st=256, sh=128, kp=k, vp=v, sm=FAKE: \
+        lib.nbx_paged_kv_append(nk, nv, dt, n, st, sh, ctypes.byref(kp) if kp else None,
+                                ctypes.byref(vp) if vp else None, sm, None, None)
+    assert f(nk=None) == -1
+    assert f(sm=None) == -1
+    assert f(vp=None) == -1                      # new_v given without a V pool
+    assert f(dt=2) == -2
+    assert f(sh=64) == -3
+    assert f(st=260) == -4
+    assert f(nk=FAKE + 8) == -4
+    assert f(vp=pool(num_pages=9)) == -3
+    assert f(n=0) == 0                           # no-op, nothing launched
+
+
+def test_merge_validation(lib):
+    m = lambda o=FAKE, out=FAKE, rows=4, ns=2, D=128, dt=0: lib.nbx_paged_decode_merge(
+        o, FAKE, FAKE, rows, ns, D, out, dt, None)
+    assert m(o=None) == -1
+    assert m(dt=2) == -2
+    assert m(D=100) == -3
+    assert m(ns=0) == -3
+    assert m(out=FAKE + 2) == -4
+
+
+def test_one_call_workspace_checks(lib):
+    k, v = pool(), pool()
+    call = lambda ws, nbytes: lib.nbx_paged_decode(
+        FAKE, 1, 2, 4, 1, 0, ctypes.byref(k), ctypes.byref(v), FAKE, 4, FAKE, 0.1, 256, 2, ws,
+        nbytes, FAKE, 0, None, None)
+    need = nb.nbx_paged_decode_workspace_bytes(8, 2, 128)
+    assert call(None, need) == -5
+    assert call(FAKE, need - 1) == -5
+    assert call(FAKE + 16, need) == -5

@@ -1,0 +1,273 @@
+"""GPU parity: the library (through its C ABI) against the float64 oracle.
+
+Every case is seeded synthetic input with NaN in every pool slot no sequence
+position uses, so a read of the wrong slot poisons the output.  Tolerances
+are max-abs against the oracle: 1e-5 for fp32 pools, 2e-3 for bf16 and 2e-2
+for fp8 e4m3; the append and all indexing are compared bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_split_kv_append_amd import synth
+
+from gpu_cases import TOL, DevCase, max_abs
+
+pytestmark = pytest.mark.gpu
+
+# oracle-sized versions of the five workloads: several splits and tiles, ragged tails
+REDUCED = {
+    1: dict(),
+    2: dict(batch=6, lens=("uniform", 1, 700)),
+    3: dict(batch=2, lens=("uniform", 300, 900)),
+    4: dict(lens=("fixed", 1000)),
+    5: dict(batch=3, lens=("loguniform", 100, 3000)),
+}
+
+
+def _reference(case, dc):
+    """Oracle output for the case after its append (if any)."""
+    if case.new_k is not None:
+        kp, vp, bad = oracle.case_append(case)
+        assert bad == 0
+    else:
+        kp, vp = case.k_pool, case.v_pool
+    return oracle.attention(case.q, case.q_dtype, kp, vp, case.kv_dtype, case.block_table,
+                            case.seq_lens, case.softmax_scale, case.causal, case.k_scale,
+                            case.v_scale), kp, vp
+
+
+def _pool_bits(t: torch.Tensor) -> np.ndarray:
+    """Raw bytes of a pool (NaN-safe bit comparison)."""
+    return t.detach().cpu().contiguous().view(torch.uint8).numpy().reshape(-1)
+
+
+def _bytes(a: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(a).view(np.uint8).reshape(-1)
+
+
+@pytest.mark.parametrize("workload", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("seed", [None, 101])
+def test_decode_matches_oracle(workload, seed):
+    case = synth.make_case(workload, seed=seed, **REDUCED[workload])
+    print(f"case workload={workload} seed={seed} {case.name} lens={case.seq_lens.tolist()[:8]}",
+          flush=True)
+    dc = DevCase(case)
+    if case.new_k is not None:
+        dc.append()
+    out = dc.decode()
+    torch.cuda.synchronize()
+    ref, _, _ = _reference(case, dc)
+    assert dc.err_bits() == 0
+    assert torch.isfinite(out).all()
+    err = max_abs(out, ref)
+    assert err <= TOL[case.kv_dtype], f"max abs err {err}"
+
+
+@pytest.mark.parametrize("workload", [2, 5])
+def test_append_is_bit_exact(workload):
+    case = synth.make_case(workload, seed=7, **REDUCED[workload])
+    dc = DevCase(case)
+    dc.append()
+    torch.cuda.synchronize()
+    kp, vp, bad = oracle.case_append(case)
+    assert bad == 0 and dc.err_bits() == 0
+    assert np.array_equal(_pool_bits(dc.k), _bytes(kp))
+    assert np.array_equal(_pool_bits(dc.v), _bytes(vp))
+
+
+@pytest.mark.parametrize("pool_dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("src", [torch.float32, torch.bfloat16])
+def test_append_casts_bit_exact(pool_dtype, src):
+    g = torch.Generator().manual_seed(3)
+    P, H, T, D, n = 5, 2, 16, 64, 9
+    pool = {"f32": torch.zeros(P, H, T, D), "bf16": torch.zeros(P, H, T, D, dtype=torch.bfloat16),
+            "fp8": torch.zeros(P, H, T, D, dtype=torch.uint8)}[pool_dtype]
+    new = (torch.randn(n, H, D, generator=g) * 3).to(src)
+    new[0, 0, :4] = torch.tensor([float("nan"), 1e-40, 500.0, -2.0 ** -10])
+    slots = torch.tensor([0, 17, -1, 33, 79, 50, 2, 64, 31], dtype=torch.int32)
+    scale = 0.037 if pool_dtype == "fp8" else 1.0
+    from paged_split_kv_append_amd import binding as nb
+    pk = pool.clone().cuda()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    nb.nbx_paged_kv_append(new.cuda(), None, nb.KVPool(pk, scale), None, slots.cuda(),
+                           dev_err=err)
+    torch.cuda.synchronize()
+    ref, bad = oracle.append(new, "f32" if src == torch.float32 else "bf16", pool, pool_dtype,
+                             scale, T, slots.numpy())
+    assert bad == 0 and int(err.item()) == 0
+    assert np.array_equal(_pool_bits(pk), _bytes(ref))
+
+
+def test_append_flags_out_of_range_and_skips_negative():
+    from paged_split_kv_append_amd import binding as nb
+    P, H, T, D = 2, 1, 16, 64
+    pool = torch.full((P, H, T, D), 7.0, device="cuda")
+    new = torch.ones(3, H, D, device="cuda")
+    slots = torch.tensor([-5, 32, 40], dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    nb.nbx_paged_kv_append(new, None, nb.KVPool(pool), None, slots, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == nb.DEVERR_SLOT_RANGE
+    assert torch.all(pool == 7.0)
+
+
+@pytest.mark.parametrize("workload", [2, 3, 4, 5])
+def test_partials_match_oracle(workload):
+    case = synth.make_case(workload, seed=11, append=False, **REDUCED[workload])
+    dc = DevCase(case)
+    S = 64
+    n = -(-int(case.seq_lens.max()) // S) + 1          # one trailing empty split
+    o, m, l = dc.partial(n, S)
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle.partials(case.q, case.q_dtype, case.k_pool, case.v_pool, case.kv_dtype,
+                                 case.block_table, case.seq_lens, case.softmax_scale, S, n,
+                                 case.causal, case.k_scale, case.v_scale)
+    m_np, l_np, o_np = m.cpu().double().numpy(), l.cpu().double().numpy(), o.cpu().double().numpy()
+    empty = rm == -np.inf
+    assert np.all(m_np[empty] == -np.inf) and np.all(l_np[empty] == 0) and np.all(o_np[empty] == 0)
+    ne = ~empty
+    assert np.all(np.abs(m_np[ne] - rm[ne]) <= 1e-5 * np.maximum(1, np.abs(rm[ne])))
+    # compare o / l (the normalised split output), robust to the split's own max
+    tol = TOL[case.kv_dtype]
+    assert np.max(np.abs(o_np[ne] / l_np[ne][:, None] - ro[ne] / rl[ne][:, None])) <= tol
+    assert np.max(np.abs(l_np[ne] - rl[ne]) / rl[ne]) <= 10 * tol
+
+
+def test_merge_matches_oracle_on_oracle_partials():
+    rng = np.random.default_rng(5)
+    rows, ns, D = 37, 9, 128
+    m = rng.normal(size=(rows, ns)) * 5
+    m[:, 3] = -np.inf
+    m[4] = -np.inf                                     # a row with no visible key
+    l = np.where(m == -np.inf, 0.0, rng.uniform(1, 50, size=(rows, ns)))
+    o = rng.normal(size=(rows, ns, D)) * l[:, :, None]
+    m32, l32, o32 = (np.float32(x) for x in (m, l, o))
+    ref = oracle.merge(o32.astype(np.float64), m32.astype(np.float64), l32.astype(np.float64))
+    from paged_split_kv_append_amd import binding as nb
+    out = torch.empty(rows, D, device="cuda")
+    nb.nbx_paged_decode_merge(torch.from_numpy(o32).cuda(), torch.from_numpy(m32).cuda(),
+                              torch.from_numpy(l32).cuda(), out)
+    torch.cuda.synchronize()
+    assert max_abs(out, ref) <= 1e-6
+    assert torch.all(out[4] == 0)
+
+
+@pytest.mark.parametrize("workload", [2, 5])
+def test_split_count_invariance(workload):
+    case = synth.make_case(workload, seed=12, append=False, **REDUCED[workload])
+    dc = DevCase(case)
+    ref, _, _ = _reference(case, dc)
+    L = int(case.seq_lens.max())
+    for S in (16, 256, 2048):
+        out = dc.decode(-(-L // S), S)
+        torch.cuda.synchronize()
+        assert max_abs(out, ref) <= TOL[case.kv_dtype], S
+
+
+@pytest.mark.parametrize("workload", [2, 3])
+def test_page_placement_is_bitwise_invariant(workload):
+    case = synth.make_case(workload, seed=13, append=False, **REDUCED[workload])
+    a = DevCase(case).decode()
+    P = case.num_pages
+    perm = np.random.default_rng(1).permutation(P)
+    k2 = torch.empty_like(case.k_pool)
+    v2 = torch.empty_like(case.v_pool)
+    k2[perm] = case.k_pool
+    v2[perm] = case.v_pool
+    case.k_pool, case.v_pool = k2, v2
+    case.block_table = np.where(case.block_table >= 0,
+                                perm[np.maximum(case.block_table, 0)], -1).astype(np.int32)
+    b = DevCase(case).decode()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("workload", [2, 4])
+def test_repeated_runs_are_bitwise_identical(workload):
+    case = synth.make_case(workload, seed=14, append=False, **REDUCED[workload])
+    dc = DevCase(case)
+    outs = [dc.decode().clone() for _ in range(5)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+
+
+def test_bf16_output_within_tolerance_plus_half_ulp():
+    case = synth.make_case(2, seed=15, append=False, **REDUCED[2])
+    dc = DevCase(case)
+    out = dc.decode(out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref, _, _ = _reference(case, dc)
+    half_ulp = np.abs(ref) * 2.0 ** -9 + 1e-30
+    err = np.abs(out.double().cpu().numpy() - ref)
+    assert np.all(err <= TOL["bf16"] + half_ulp)
+
+
+def test_interleaved_kv_allocation_gives_identical_bits():
+    """K and V as strided views of one [P, 2, H, T, D] allocation."""
+    case = synth.make_case(2, seed=16, append=False, **REDUCED[2])
+    a = DevCase(case).decode()
+    both = torch.stack([case.k_pool, case.v_pool], dim=1).cuda()
+    dc = DevCase(case)
+    dc.k, dc.v = both[:, 0], both[:, 1]
+    b = dc.decode()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_bad_page_sets_flag_and_stays_finite():
+    case = synth.make_case(2, seed=17, append=False, batch=2, lens=("fixed", 100))
+    case.block_table[1, 2] = -1
+    dc = DevCase(case)
+    out = dc.decode()
+    torch.cuda.synchronize()
+    from paged_split_kv_append_amd import binding as nb
+    assert dc.err_bits() & nb.DEVERR_PAGE_RANGE
+    assert torch.isfinite(out).all()
+    # the sequence without a bad page is unaffected
+    ref, _, _ = _reference(synth.make_case(2, seed=17, append=False, batch=2, lens=("fixed", 100)),
+                           dc)
+    G = case.q_heads
+    assert max_abs(out[:G], ref[:G]) <= TOL["bf16"]
+
+
+def test_zero_length_sequence_gives_zero_rows():
+    case = synth.make_case(2, seed=18, append=False, batch=3, lens=("fixed", 50))
+    case.seq_lens[1] = 0
+    dc = DevCase(case)
+    out = dc.decode()
+    torch.cuda.synchronize()
+    H = case.q_heads
+    assert torch.all(out[H:2 * H] == 0)
+    ref = oracle.attention(case.q, case.q_dtype, case.k_pool, case.v_pool, case.kv_dtype,
+                           case.block_table, case.seq_lens, case.softmax_scale)
+    assert max_abs(out, ref) <= TOL["bf16"]
+
+
+# ------------------------------------------------------------------ full sizes
+
+FULL_ROWS = {2: None, 5: None, 3: [(0, 48), (1488, 1536)], 4: [(0, 32), (3040, 3072)]}
+
+
+@pytest.mark.parametrize("workload", [2, 3, 4, 5])
+def test_full_size_against_oracle(workload):
+    case = synth.make_case(workload)
+    print(f"full-size workload={workload} kv_bytes={case.kv_bytes()}", flush=True)
+    dc = DevCase(case)
+    if case.new_k is not None:
+        dc.append()
+    out = dc.decode()
+    torch.cuda.synchronize()
+    assert dc.err_bits() == 0
+    assert torch.isfinite(out).all()
+    if case.new_k is not None:
+        kp, vp, _ = oracle.case_append(case)
+    else:
+        kp, vp = case.k_pool, case.v_pool
+    ranges = FULL_ROWS[workload] or [(0, case.rows)]
+    for r0, r1 in ranges:
+        ref = oracle.attention(case.q, case.q_dtype, kp, vp, case.kv_dtype, case.block_table,
+                               case.seq_lens, case.softmax_scale, case.causal, case.k_scale,
+                               case.v_scale, rows=(r0, r1))
+        err = max_abs(out[r0:r1], ref[r0:r1])
+        assert err <= TOL[case.kv_dtype], (r0, r1, err)
