@@ -201,9 +201,17 @@ int oracle_append(const void *new_vals, int src, int64_t n_tok, int h_kv, int d,
         pos = slot % page_tokens;
         for (int h = 0; h < h_kv; ++h)
             for (int e = 0; e < d; ++e) {
-                double x = oracle_decode_value(src, new_vals, (t * h_kv + h) * (int64_t)d + e);
+                int64_t src_i = (t * h_kv + h) * (int64_t)d + e;
                 int64_t dst_i = ((page * h_kv + h) * (int64_t)page_tokens + pos) * d + e;
-                oracle_encode_value(dst, x, scale, pool, dst_i);
+                if (src == dst && dst != ORC_E4M3) {
+                    /* a cast to the element's own type leaves its bits alone,
+                     * NaN payloads included */
+                    size_t sz = elem_size(dst);
+                    memcpy((char *)pool + dst_i * sz, (const char *)new_vals + src_i * sz, sz);
+                    continue;
+                }
+                oracle_encode_value(dst, oracle_decode_value(src, new_vals, src_i), scale, pool,
+                                    dst_i);
             }
     }
     return bad;

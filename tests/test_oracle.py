@@ -152,6 +152,14 @@ def test_append_worked_example():
     assert np.array_equal(out, expect)
 
 
+def test_append_same_dtype_copies_bits_including_nan_payloads():
+    new = np.array([[[0x7FFF, 0xFFC1, 0x3F80, 0x0001]]], np.uint16)   # two NaN payloads
+    pool = np.zeros((1, 1, 16, 4), np.uint16)
+    out, _ = oracle.append(new, "bf16", pool, "bf16", 1.0, 16, np.array([3], np.int32))
+    assert np.array_equal(out.reshape(16, 4)[3], new[0, 0])
+    assert np.all(out.reshape(16, 4)[[0, 1, 2, 4]] == 0)
+
+
 def test_append_casts_like_the_library_casts():
     rng = np.random.default_rng(4)
     new = rng.standard_normal((3, 2, 8)).astype(np.float32)
