@@ -247,7 +247,10 @@ int nbx_paged_decode_partial(const void *q, int32_t q_dtype, int32_t batch, int3
     a.m_part = m_part;
     a.l_part = l_part;
     a.dev_err = dev_err;
-    return to_status(nbx::launch_partial_valu(a, stream));
+    // matrix cores for 16/8-bit pools read with bf16 Q; the vector-ALU kernel
+    // for fp32 pools and fp32 Q
+    const bool mfma = q_dtype == NBX_BF16 && (a.kv_dtype == NBX_BF16 || a.kv_dtype == NBX_FP8_E4M3);
+    return to_status(mfma ? nbx::launch_partial_mfma(a, stream) : nbx::launch_partial_valu(a, stream));
 }
 
 int nbx_paged_decode_merge(const float *o_part, const float *m_part, const float *l_part,

@@ -54,6 +54,7 @@ struct MergeArgs {
 
 hipError_t launch_append(const AppendArgs &a, hipStream_t stream);
 hipError_t launch_partial_valu(const PartialArgs &a, hipStream_t stream);
+hipError_t launch_partial_mfma(const PartialArgs &a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t stream);
 
 }  // namespace nbx

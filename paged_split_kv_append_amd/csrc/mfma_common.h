@@ -1,0 +1,120 @@
+// MFMA helpers for the 16-bit / 8-bit pool kernels (gfx950).
+//
+// Operand layout of v_mfma_f32_16x16x32_bf16 (lane l = 16 g + j, g = l / 16):
+//   A (16 x 32): lane holds A[j][8 g + t], t = 0..7
+//   B (32 x 16): lane holds B[8 g + t][j]
+//   C (16 x 16): lane holds C[4 g + i][j], i = 0..3
+// ds_read_tr16_b64: in each 16-lane group, lane j pointing at row 4 g' + j/4,
+// column c0 + 4 (j % 4) of a row-major 16-bit tile receives the four elements
+// of column c0 + j in rows 4 g' .. 4 g' + 3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+
+namespace nbx {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// E4M3FN code (low byte of c) -> bf16 bits, exact.  The 7 magnitude bits are
+// placed as the exponent/mantissa of an fp32 with bias 127 instead of 7 and the
+// value rescaled by 2^120 (subnormal codes become fp32 denormals, which the
+// multiply keeps); at most 4 significant bits, so the top half is the bf16.
+__device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t c)
+{
+    const uint32_t em = c & 0x7Fu;
+    const float f = __uint_as_float(em << 20) * 0x1p120f;
+    uint32_t b = __float_as_uint(f) >> 16;
+    b = em == 0x7Fu ? 0x7FC0u : b;
+    return b | ((c & 0x80u) << 8);
+}
+
+// 8 consecutive elements of a pool row at element index i, as 8 bf16 (4 dwords)
+template <int KVT>
+__device__ __forceinline__ u32x4 load8_bf16(const void *base, int64_t i)
+{
+    if constexpr (KVT == NBX_BF16) {
+        return *(const u32x4 *)((const uint16_t *)base + i);
+    } else {
+        const u32x2 w = *(const u32x2 *)((const uint8_t *)base + i);
+        u32x4 r;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const uint32_t x = w[k];
+            r[2 * k] = e4m3_to_bf16_bits(x & 0xFFu) | (e4m3_to_bf16_bits((x >> 8) & 0xFFu) << 16);
+            r[2 * k + 1] =
+                e4m3_to_bf16_bits((x >> 16) & 0xFFu) | (e4m3_to_bf16_bits(x >> 24) << 16);
+        }
+        return r;
+    }
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
+{
+    const __bf16 a = (__bf16)lo, b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ float bf16_round(float x)
+{
+    return (float)(__bf16)x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x)
+{
+    return __builtin_amdgcn_exp2f(x);
+}
+
+// A-operand of the P V product (V^T, 16 columns of V x 32 positions) from a
+// row-major bf16 tile in LDS: rows are positions, `stride` bytes apart.
+// Lane 16 g + j gets V[4 g + t][c0 + j] (t = 0..3) and V[16 + 4 g + t][c0 + j].
+__device__ __forceinline__ u32x4 lds_vt_operand(const uint8_t *tile, int stride, int c0, int lane)
+{
+    const int g = lane >> 4, j = lane & 15;
+    const uint8_t *p0 = tile + (4 * g + (j >> 2)) * stride + (c0 + 4 * (j & 3)) * 2;
+    const uint8_t *p1 = p0 + 16 * stride;
+    const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4 *)(__attribute__((address_space(3))) uint8_t *)p0);
+    const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4 *)(__attribute__((address_space(3))) uint8_t *)p1);
+    const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+    return u32x4{ua[0], ua[1], ub[0], ub[1]};
+}
+
+__device__ __forceinline__ float xor_max16_32(float v)
+{
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+
+__device__ __forceinline__ float xor_sum16_32(float v)
+{
+    v += __shfl_xor(v, 16, 64);
+    return v + __shfl_xor(v, 32, 64);
+}
+
+// Hardware workgroup id -> logical id such that each of the 8 XCDs (which
+// receive workgroups round-robin) gets one contiguous range of logical ids.
+__device__ __forceinline__ uint32_t xcd_contiguous_id(uint32_t hw, uint32_t n)
+{
+    const uint32_t per = n / 8, rem = n % 8;
+    const uint32_t xcd = hw % 8, slot = hw / 8;
+    return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+}
+
+}  // namespace nbx
