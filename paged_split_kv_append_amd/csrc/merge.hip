@@ -1,10 +1,16 @@
 // Fixed-order combine of split partials (nbxtensor attention_wrappers.py,
-// decode_reduce: one program per query row, partials in split order).
+// decode_reduce: one program per query row, partials combined in a fixed
+// order so the result does not depend on scheduling).
 //
 // Per row: M = the largest m_s over non-empty splits (m_s = -inf marks an
-// empty one), w_s = exp(m_s - M), out = sum_s w_s o_s / sum_s w_s l_s with s
-// ascending.  One wave per row; each lane owns D/64 consecutive elements so
-// the o_s rows are read with coalesced vector loads.
+// empty one), w_s = exp(m_s - M), out = sum_s w_s o_s / sum_s w_s l_s.
+//
+// One workgroup of 4 waves per row.  The lanes first take the splits 64 at a
+// time to form M, the weights w_s (kept in LDS) and the denominator by a
+// butterfly sum; then wave k accumulates w_s o_s over the splits s = k, k + 4,
+// ... in ascending order, with 8 independent loads in flight, each lane owning
+// D/64 consecutive elements; the four wave sums are added in order 0..3.  The
+// order is fixed, so repeated runs give identical bits.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -12,77 +18,98 @@ namespace nbx {
 
 namespace {
 
+constexpr int kMaxSplitsMerge = 4096;
+
 template <int D, int OUT>
 __global__ void __launch_bounds__(256)
 merge_kernel(MergeArgs a)
 {
     constexpr int E = D / 64;
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= a.rows)
-        return;
+    __shared__ float w_s[kMaxSplitsMerge];
+    __shared__ float red[4][D];
+    __shared__ float stat[2];                  // M, den
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t row = blockIdx.x;
     const int ns = a.n_split;
     const float *m = a.m_part + row * ns;
     const float *l = a.l_part + row * ns;
-    const float *o = a.o_part + row * (int64_t)ns * D + lane * E;
 
-    float M = -INFINITY;
-    bool has_nan = false;
-    for (int s = 0; s < ns; ++s) {
-        const float ms = m[s];
-        has_nan |= ms != ms;
-        M = fmaxf(M, ms);
+    if (wv == 0) {
+        float M = -INFINITY;
+        bool has_nan = false;
+        for (int s = lane; s < ns; s += 64) {
+            const float ms = m[s];
+            has_nan |= ms != ms;
+            M = fmaxf(M, ms);
+        }
+        M = wave_max(M);
+        has_nan = __any(has_nan);
+        float den = 0.0f;
+        for (int s = lane; s < ns; s += 64) {
+            const float ms = m[s];
+            const float w = (ms == -INFINITY || M == -INFINITY) ? 0.0f
+                                                                 : exp2f((ms - M) * kLog2e);
+            w_s[s] = w;
+            den = fmaf(w, l[s], den);
+        }
+        den = wave_sum(den);
+        if (lane == 0) {
+            stat[0] = has_nan ? __builtin_nanf("") : M;
+            stat[1] = den;
+        }
     }
+    __syncthreads();
+
     float acc[E];
 #pragma unroll
     for (int k = 0; k < E; ++k)
         acc[k] = 0.0f;
-    float den = 0.0f;
-    if (M != -INFINITY) {
-        for (int s = 0; s < ns; ++s) {
-            const float ms = m[s];
-            if (ms == -INFINITY)
-                continue;
-            const float w = exp2f((ms - M) * kLog2e);
-            den = fmaf(w, l[s], den);
-            const float *os = o + (int64_t)s * D;
-            if constexpr (E == 4) {
-                const float4 v = *(const float4 *)os;
-                acc[0] = fmaf(w, v.x, acc[0]);
-                acc[1] = fmaf(w, v.y, acc[1]);
-                acc[2] = fmaf(w, v.z, acc[2]);
-                acc[3] = fmaf(w, v.w, acc[3]);
-            } else if constexpr (E == 2) {
-                const float2 v = *(const float2 *)os;
-                acc[0] = fmaf(w, v.x, acc[0]);
-                acc[1] = fmaf(w, v.y, acc[1]);
-            } else {
-                acc[0] = fmaf(w, os[0], acc[0]);
-            }
+    const float *o = a.o_part + row * (int64_t)ns * D + lane * E;
+    int s = wv;
+    for (; s + 28 < ns; s += 32) {             // 8 splits of this wave per batch
+        float v[8][E];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float *os = o + (int64_t)(s + 4 * u) * D;
+#pragma unroll
+            for (int k = 0; k < E; ++k)
+                v[u][k] = os[k];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float w = w_s[s + 4 * u];
+#pragma unroll
+            for (int k = 0; k < E; ++k)
+                acc[k] = fmaf(w, v[u][k], acc[k]);
         }
     }
-    float res[E];
+    for (; s < ns; s += 4) {
+        const float w = w_s[s];
+        const float *os = o + (int64_t)s * D;
+#pragma unroll
+        for (int k = 0; k < E; ++k)
+            acc[k] = fmaf(w, os[k], acc[k]);
+    }
 #pragma unroll
     for (int k = 0; k < E; ++k)
-        res[k] = has_nan ? __builtin_nanf("") : (den > 0.0f ? acc[k] / den : 0.0f);
+        red[wv][lane * E + k] = acc[k];
+    __syncthreads();
 
-    if constexpr (OUT == NBX_F32) {
-        float *dst = (float *)a.out + row * D + lane * E;
-#pragma unroll
-        for (int k = 0; k < E; ++k)
-            dst[k] = res[k];
-    } else {
-        uint16_t *dst = (uint16_t *)a.out + row * D + lane * E;
-#pragma unroll
-        for (int k = 0; k < E; ++k)
-            dst[k] = f32_to_bf16_bits(res[k]);
+    const float M = stat[0], den = stat[1];
+    for (int e = threadIdx.x; e < D; e += 256) {
+        float r = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
+        r = M != M ? __builtin_nanf("") : (den > 0.0f ? r / den : 0.0f);
+        if constexpr (OUT == NBX_F32)
+            ((float *)a.out)[row * D + e] = r;
+        else
+            ((uint16_t *)a.out)[row * D + e] = f32_to_bf16_bits(r);
     }
 }
 
 template <int OUT>
 hipError_t launch_out(const MergeArgs &a, hipStream_t stream)
 {
-    dim3 grid((unsigned)((a.rows + 3) / 4));
+    dim3 grid((unsigned)a.rows);
     switch (a.head_dim) {
     case 64: hipLaunchKernelGGL((merge_kernel<64, OUT>), grid, dim3(256), 0, stream, a); break;
     case 128: hipLaunchKernelGGL((merge_kernel<128, OUT>), grid, dim3(256), 0, stream, a); break;
@@ -92,6 +119,8 @@ hipError_t launch_out(const MergeArgs &a, hipStream_t stream)
 }
 
 }  // namespace
+
+int merge_max_splits() { return kMaxSplitsMerge; }
 
 hipError_t launch_merge(const MergeArgs &a, hipStream_t stream)
 {

@@ -22,7 +22,36 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// Raw buffer access (gfx9 buffer descriptors): base address and byte range in
+// scalar registers, per-lane 32-bit offsets.  A lane whose access falls
+// outside the range reads zeros and touches no memory.
+__device__ u32x4 nbx_buffer_load_b128(i32x4 rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.v4i32");
+__device__ u32x2 nbx_buffer_load_b64(i32x4 rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.v2i32");
+__device__ void nbx_buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) void *lds,
+                                    int size, int voffset, int soffset, int imm_offset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// Descriptor for `bytes` bytes from `base` (uniform values; forced to SGPRs).
+__device__ __forceinline__ i32x4 make_buffer_rsrc(const void *base, uint32_t bytes)
+{
+    const uint64_t a = (uint64_t)base;
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFFu));
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+
+// 8 consecutive pool elements at byte offset `voff` of a buffer, as 8 bf16
+template <int KVT>
+__device__ __forceinline__ u32x4 buffer_load8_bf16(i32x4 rsrc, int voff);
 
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c)
 {
@@ -61,6 +90,26 @@ __device__ __forceinline__ u32x4 load8_bf16(const void *base, int64_t i)
         }
         return r;
     }
+}
+
+template <>
+__device__ __forceinline__ u32x4 buffer_load8_bf16<NBX_BF16>(i32x4 rsrc, int voff)
+{
+    return nbx_buffer_load_b128(rsrc, voff, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ u32x4 buffer_load8_bf16<NBX_FP8_E4M3>(i32x4 rsrc, int voff)
+{
+    const u32x2 w = nbx_buffer_load_b64(rsrc, voff, 0, 0);
+    u32x4 r;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const uint32_t x = w[k];
+        r[2 * k] = e4m3_to_bf16_bits(x & 0xFFu) | (e4m3_to_bf16_bits((x >> 8) & 0xFFu) << 16);
+        r[2 * k + 1] = e4m3_to_bf16_bits((x >> 16) & 0xFFu) | (e4m3_to_bf16_bits(x >> 24) << 16);
+    }
+    return r;
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)

@@ -13,27 +13,43 @@
 //   S^T (16 positions x 16 rows) = K (16 x D) . Q^T (D x 16)
 //   O^T (16 columns x 16 rows) += V^T (16 x 32 positions) . P^T (32 x 16)
 // so that every lane owns one query row (its column) in both S^T and O^T and
-// the softmax bookkeeping never leaves the lane's row.  K rows feed the A
-// operand straight from 16-byte loads; V goes through LDS and is transposed
-// by the LDS transpose read.  bf16 K/V products are exact; P is rounded to
-// bf16 for the P V product, and for bf16 pools its rounding residual is
-// multiplied in a second MFMA (P = hi + lo, relative error ~2^-17).  fp8 codes
-// are widened to bf16 exactly; their per-tensor scales are applied to the
-// scores (K) and to nothing else until the merge sees o (V scale folded into
-// o here).  Scores are kept in log2 units.
+// the softmax bookkeeping never leaves the lane's row.  bf16 K/V products are
+// exact; P is rounded to bf16 for the P V product, and for bf16 pools the
+// rounding residual is multiplied in a second MFMA (P = hi + lo, relative
+// error about 2^-17).  fp8 codes are widened to bf16 exactly; the K scale is
+// folded into the score scale and the V scale into the stored o.  Scores are
+// kept in log2 units (scale * log2 e folded in); m is stored in natural units.
+//
+// Memory path.  A 32-position chunk is two 16-position tiles; a tile never
+// straddles a page (page sizes are multiples of 16 and splits start on tile
+// boundaries), so each tile is one buffer descriptor: base = the tile's first
+// row, range = the rows that hold data (0 for an unmapped page).  Lanes carry
+// fixed 32-bit offsets; out-of-range lanes read zeros and touch no memory.
+// V tiles are staged in LDS column-blocked: for each 16-column slice, the 16
+// rows x 32 bytes of a tile are one contiguous 512-byte block.  One 64-lane
+// 16-byte load (one row slice per lane pair) fills two such blocks, and the
+// LDS transpose read of a slice
+// (lane 16 g + j: row 4 g + j/4, 8 bytes at column 4 (j % 4)) touches 512
+// consecutive bytes, so it is free of bank conflicts and every slice is a
+// constant offset from one per-lane address.  Page ids come from the block
+// table once per 32 chunks (one per lane) and are broadcast with readlane.
 //
 // Two kernels:
 //  - decode_mfma_kernel: at most 16 rows per KV head (decode, short windows).
-//    One workgroup of 4 waves per (split, sequence x KV head); the waves take
-//    interleaved 32-position chunks of the split, each with its own running
-//    (m, l, O), and combine them in a fixed order at the end.  K goes from HBM
-//    into MFMA operand registers; each wave stages its V chunk in private LDS.
-//    The next chunk's loads are issued before the current one is computed.
+//    PG waves per (split, sequence x KV head) take interleaved chunks of the
+//    split, each with its own (m, l, O), combined in a fixed order at the end.
+//    K rows go from HBM straight into MFMA operand registers; V rows are
+//    loaded into registers and written to the wave's LDS tile once they land
+//    (fp8 codes widened on the way).  The wave's next chunk is loaded while
+//    the current one is computed.
 //  - multirow_mfma_kernel: more rows per KV head (verify windows, prompt
 //    chunks).  A workgroup takes RW x NT row tiles of 16 rows; its waves share
-//    each K/V chunk through LDS (K XOR-swizzled for conflict-free operand
-//    reads).  Workgroups are ordered row block fastest and mapped so that the
-//    row blocks of one split land on the same XCD and share its L2.
+//    the loads of each K and V chunk and stage it in LDS (K column-blocked by
+//    64 bytes, which makes the operand reads conflict-free too); the next
+//    chunk is in registers while the current one is computed.
+//    Workgroups are ordered row block fastest and mapped so that the row
+//    blocks of one split run on the same XCD and share its L2 (the rows-first
+//    order of TensorFold PR #1219, made XCD-aware).
 #include "kernels.h"
 #include "mfma_common.h"
 
@@ -41,12 +57,7 @@ namespace nbx {
 
 namespace {
 
-constexpr int kChunk = 32;   // positions per chunk: two 16-position S tiles, one PV k-step
-
-template <int KVT, int UPT>
-struct Loaded {
-    u32x4 u[UPT];
-};
+constexpr int kChunk = 32;   // positions per chunk: two 16-position tiles, one PV k-step
 
 __device__ __forceinline__ int clamp_len(const PartialArgs &a, int b, bool flag_it)
 {
@@ -74,6 +85,60 @@ __device__ __forceinline__ int tile_page(const PartialArgs &a, int b, int ts, in
         return -1;
     }
     return page;
+}
+
+// Lane i of the result: page of tile (i & 1) of chunk c0 + (i / 2) * cstep,
+// -1 past the split.  Refreshed once per 32 chunks of a wave.
+__device__ __forceinline__ int chunk_pages(const PartialArgs &a, int b, int j0, int jend,
+                                           int nchunk, int c0, int cstep, int lane, bool flag_it)
+{
+    const int cq = c0 + (lane >> 1) * cstep;
+    const int ts = j0 + cq * kChunk + 16 * (lane & 1);
+    return cq < nchunk ? tile_page(a, b, ts, jend, flag_it) : -1;
+}
+
+// Buffer descriptor of tile rows [0, rows) starting at position ts in `page`
+// (rows <= 0 or an unmapped page gives an empty range).
+template <int ESZ>
+__device__ __forceinline__ i32x4 tile_rsrc(const void *data, int64_t stride_page,
+                                           int64_t head_off, int64_t stride_token, int page_tokens,
+                                           int page, int ts, int rows)
+{
+    const int pg = page >= 0 ? page : 0;
+    const int64_t off = (int64_t)(ts % page_tokens);
+    const uint8_t *base =
+        (const uint8_t *)data + ((int64_t)pg * stride_page + head_off + off * stride_token) * ESZ;
+    const uint32_t bytes = page >= 0 && rows > 0 ? (uint32_t)(rows * stride_token * ESZ) : 0u;
+    return make_buffer_rsrc(base, bytes);
+}
+
+// A operand of the P V product for 16-column slice dt from a column-blocked
+// chunk tile (tile 0 blocks, then tile 1 blocks); `lane_base` is the lane's
+// fixed address: block 0 of tile 0 + (4 g + j/4) * 32 + (j % 4) * 8.
+template <int DT>
+__device__ __forceinline__ u32x4 vt_operand(const uint8_t *lane_base, int dt)
+{
+    const uint8_t *p0 = lane_base + dt * 512;
+    const uint8_t *p1 = p0 + DT * 512;
+    const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4 *)(__attribute__((address_space(3))) uint8_t *)p0);
+    const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4 *)(__attribute__((address_space(3))) uint8_t *)p1);
+    const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+    return u32x4{ua[0], ua[1], ub[0], ub[1]};
+}
+
+// 8 E4M3FN codes (two dwords) widened to 8 bf16 (four dwords), exactly
+__device__ __forceinline__ u32x4 widen8_e4m3(u32x2 w)
+{
+    u32x4 r;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const uint32_t x = w[k];
+        r[2 * k] = e4m3_to_bf16_bits(x & 0xFFu) | (e4m3_to_bf16_bits((x >> 8) & 0xFFu) << 16);
+        r[2 * k + 1] = e4m3_to_bf16_bits((x >> 16) & 0xFFu) | (e4m3_to_bf16_bits(x >> 24) << 16);
+    }
+    return r;
 }
 
 // Online-softmax step for one lane's row over the 32 positions of a chunk:
@@ -120,52 +185,22 @@ __device__ __forceinline__ void softmax_step(float (&sc)[2][4], float &m_run, fl
 
 // ------------------------------------------------------------------ decode
 
-// Swizzle of the 16-byte units of V tile row r: unit U of the row is stored at
-// U ^ vswz(r), so that the 16 rows read by one transposed read spread over all
-// LDS banks.
-template <int UPR>
-__device__ __forceinline__ int vswz(int r)
-{
-    return (2 * r) & (UPR - 2);
-}
-
-// Byte address in a swizzled [32 x D] bf16 V tile of the A operand of the P V
-// product for column tile dt: lane 16 g + j reads 4 elements of rows
-// 16 h + 4 g + j/4, columns 16 dt + 4 (j % 4) .. + 3.
-template <int D>
-__device__ __forceinline__ u32x4 lds_vt_operand_swz(const uint8_t *tile, int dt, int lane)
-{
-    constexpr int UPR = D / 8;
-    const int g = lane >> 4, j = lane & 15;
-    const int U = 2 * dt + ((j >> 1) & 1);
-    const int r0 = 4 * g + (j >> 2), r1 = r0 + 16;
-    const uint8_t *p0 = tile + r0 * (2 * D) + ((U ^ vswz<UPR>(r0)) * 16) + 8 * (j & 1);
-    const uint8_t *p1 = tile + r1 * (2 * D) + ((U ^ vswz<UPR>(r1)) * 16) + 8 * (j & 1);
-    const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (lds_bf16x4 *)(__attribute__((address_space(3))) uint8_t *)p0);
-    const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (lds_bf16x4 *)(__attribute__((address_space(3))) uint8_t *)p1);
-    const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
-    return u32x4{ua[0], ua[1], ub[0], ub[1]};
-}
-
-// PG waves per (split, sequence x KV head); wave w takes chunks w, w + PG, ...
 template <int D, int KVT, bool PVS, int PG>
 __global__ void __launch_bounds__(PG * 64)
 decode_mfma_kernel(PartialArgs a)
 {
     constexpr int KK = D / 32;                 // 32-wide k-steps of Q K^T
-    constexpr int DT = D / 16;                 // 16-column tiles of O
-    constexpr int UPR = D / 8;                 // 16-byte (8-element) units per V row
-    constexpr int RPI = 64 / UPR;              // V rows per 64-lane load
-    constexpr int VU = kChunk / RPI;           // V loads per lane per chunk
-    constexpr int VBYTES = kChunk * 2 * D;     // one V tile (bf16)
+    constexpr int DT = D / 16;                 // 16-column slices of V and O
+    constexpr bool BF = KVT == NBX_BF16;
+    constexpr int ESZ = BF ? 2 : 1;
+    constexpr int VBYTES = kChunk * 2 * D;     // one chunk of V as bf16
     constexpr int CMB = PG > 1 ? PG * 16 * D * 4 : 0;
     constexpr int SMEM = (PG * VBYTES > CMB) ? PG * VBYTES : CMB;
     __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
     __shared__ float cmb_m[PG][16], cmb_l[PG][16];
 
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, uniform
     const int g = lane >> 4, j = lane & 15;
     const int s = blockIdx.x;
     const int b = blockIdx.y / a.kv_heads, gk = blockIdx.y % a.kv_heads;
@@ -202,86 +237,120 @@ decode_mfma_kernel(PartialArgs a)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
         o[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    uint8_t *vt = smem + w * VBYTES;
+
     const int64_t k_head = (int64_t)gk * a.k_stride_head;
     const int64_t v_head = (int64_t)gk * a.v_stride_head;
+    const int kst_b = (int)(a.k_stride_token * ESZ), vst_b = (int)(a.v_stride_token * ESZ);
+    // fixed per-lane byte offsets inside a tile
+    const int k_lane = j * kst_b + g * 8 * ESZ;                        // + kk * 32 * ESZ
+    const int v_lane = ((lane & 31) >> 1) * vst_b + ((lane >> 5) * 16 + (lane & 1) * 8) * ESZ;
+    uint8_t *const tile = smem + w * VBYTES;
+    const uint8_t *vt_lane = tile + (4 * g + (j >> 2)) * 32 + (j & 3) * 8;
 
-    int pg_reg = -1;                           // lane i: page of tile (i & 1) of chunk q0 + i/2
-    for (int q = 0, c = w; c < nchunk; ++q, c += PG) {
-        if ((q & 31) == 0) {
-            // page ids of this wave's next 32 chunks, one tile per lane
-            const int cq = c + (lane >> 1) * PG;
-            const int ts = j0 + cq * kChunk + 16 * (lane & 1);
-            pg_reg = cq < nchunk ? tile_page(a, b, ts, jend, true) : -1;
-        }
+    // Software pipeline over this wave's chunks c = w, w + PG, ...:
+    //   V(c) lands in LDS; V(c') is issued (c' the next chunk);
+    //   S = K(c) Q^T from registers; K(c') is issued;
+    //   softmax; O += P V(c) from LDS.
+    // One register set each for K and V: a chunk's loads are in flight while
+    // the previous chunk is computed.  The compiler places the waits.
+    int pg_reg = -1;
+    u32x4 kr[2][KK];
+    u32x4 vr[BF ? DT : 1];
+    u32x2 vraw[BF ? 1 : DT];                   // fp8: V codes awaiting widening
+    auto pages_of = [&](int q, int &pg0, int &pg1) {
+        pg0 = __builtin_amdgcn_readlane(pg_reg, 2 * (q & 31));
+        pg1 = __builtin_amdgcn_readlane(pg_reg, 2 * (q & 31) + 1);
+    };
+    auto issue_v = [&](int c, int pg0, int pg1) {
         const int p0 = j0 + c * kChunk;
-        const int page0 = __builtin_amdgcn_readlane(pg_reg, 2 * (q & 31));
-        const int page1 = __builtin_amdgcn_readlane(pg_reg, 2 * (q & 31) + 1);
-        const int64_t off0 = (int64_t)(p0 % a.page_tokens);
-        const int64_t off1 = (int64_t)((p0 + 16) % a.page_tokens);
-        const int64_t kb0 = (int64_t)page0 * a.k_stride_page + k_head + off0 * a.k_stride_token;
-        const int64_t kb1 = (int64_t)page1 * a.k_stride_page + k_head + off1 * a.k_stride_token;
-        const int64_t vb0 = (int64_t)page0 * a.v_stride_page + v_head + off0 * a.v_stride_token;
-        const int64_t vb1 = (int64_t)page1 * a.v_stride_page + v_head + off1 * a.v_stride_token;
-        const int vrows = min(kChunk, jend - p0);          // V rows holding positions < jend
-
-        // K rows straight into MFMA A operands (rows past jend are masked later)
-        u32x4 kr[2][KK];
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            kr[0][kk] = page0 >= 0 ? load8_bf16<KVT>(a.k_data, kb0 + j * a.k_stride_token +
-                                                                   kk * 32 + g * 8)
-                                   : u32x4{0, 0, 0, 0};
-            kr[1][kk] = page1 >= 0 ? load8_bf16<KVT>(a.k_data, kb1 + j * a.k_stride_token +
-                                                                   kk * 32 + g * 8)
-                                   : u32x4{0, 0, 0, 0};
-        }
-        // V rows into this wave's swizzled LDS tile; rows without data become 0
-#pragma unroll
-        for (int u = 0; u < VU; ++u) {
-            const int r = u * RPI + lane / UPR, U = lane % UPR;
-            const int t = r >> 4;
-            const int page = t ? page1 : page0;
-            const bool ok = page >= 0 && r < vrows;
-            const int64_t src = (t ? vb1 : vb0) + (r & 15) * a.v_stride_token + (U ^ vswz<UPR>(r)) * 8;
-            uint8_t *dst = vt + u * 1024;
-            if constexpr (KVT == NBX_BF16) {
-                if (ok)
-                    __builtin_amdgcn_global_load_lds(
-                        (const __attribute__((address_space(1))) void *)((const uint16_t *)a.v_data + src),
-                        (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
-                else
-                    *(u32x4 *)(dst + lane * 16) = u32x4{0, 0, 0, 0};
-            } else {
-                *(u32x4 *)(dst + lane * 16) =
-                    ok ? load8_bf16<KVT>(a.v_data, src) : u32x4{0, 0, 0, 0};
-            }
-        }
-        if constexpr (KVT == NBX_BF16)
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // V tile landed in LDS
-
-        float sc[2][4];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+            const int ts = p0 + 16 * t;
+            // rows past the data fall outside the range and read as 0
+            const i32x4 rv = tile_rsrc<ESZ>(a.v_data, a.v_stride_page, v_head, a.v_stride_token,
+                                            a.page_tokens, t ? pg1 : pg0, ts, min(16, jend - ts));
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
-                acc = mfma_bf16(kr[t][kk], qb[kk], acc);
-            const bool tv = (t ? page1 : page0) >= 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int pos = p0 + 16 * t + 4 * g + i;
-                sc[t][i] = (tv && pos < e_j) ? acc[i] * scale2 : -INFINITY;
+            for (int k = 0; k < DT / 2; ++k) {
+                const int i = t * (DT / 2) + k;
+                if constexpr (BF)
+                    vr[i] = nbx_buffer_load_b128(rv, v_lane + k * 64, 0, 0);
+                else
+                    vraw[i] = nbx_buffer_load_b64(rv, v_lane + k * 32, 0, 0);
             }
         }
-        u32x4 ph, pl;
-        softmax_step<DT, PVS>(sc, m_run, l_run, o, ph, pl);
+    };
+    auto issue_k = [&](int c, int pg0, int pg1) {
+        const int p0 = j0 + c * kChunk;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const u32x4 va = lds_vt_operand_swz<D>(vt, dt, lane);
-            o[dt] = mfma_bf16(va, ph, o[dt]);
-            if constexpr (PVS)
-                o[dt] = mfma_bf16(va, pl, o[dt]);
+        for (int t = 0; t < 2; ++t) {
+            const i32x4 rk = tile_rsrc<ESZ>(a.k_data, a.k_stride_page, k_head, a.k_stride_token,
+                                            a.page_tokens, t ? pg1 : pg0, p0 + 16 * t, 16);
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                kr[t][kk] = buffer_load8_bf16<KVT>(rk, k_lane + kk * 32 * ESZ);
+        }
+    };
+    auto land_v = [&]() {
+#pragma unroll
+        for (int i = 0; i < DT; ++i) {
+            const int t = i / (DT / 2), k = i % (DT / 2);
+            u32x4 v;
+            if constexpr (BF)
+                v = vr[i];
+            else
+                v = widen8_e4m3(vraw[i]);
+            *(u32x4 *)(tile + t * DT * 512 + k * 1024 + lane * 16) = v;
+        }
+    };
+
+    int q = 0, c = w;
+    if (c < nchunk) {
+        pg_reg = chunk_pages(a, b, j0, jend, nchunk, c, PG, lane, true);
+        int pg0, pg1;
+        pages_of(0, pg0, pg1);
+        issue_v(c, pg0, pg1);
+        issue_k(c, pg0, pg1);
+        for (;;) {
+            const int cn = c + PG;
+            const bool more = cn < nchunk;
+            const int p0 = j0 + c * kChunk;
+            const int cur0 = pg0, cur1 = pg1;
+            land_v();                          // this wave's DS operations run in order
+            if (more) {
+                if (((q + 1) & 31) == 0)
+                    pg_reg = chunk_pages(a, b, j0, jend, nchunk, cn, PG, lane, true);
+                pages_of(q + 1, pg0, pg1);
+                issue_v(cn, pg0, pg1);
+            }
+            float sc[2][4];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk)
+                    acc = mfma_bf16(kr[t][kk], qb[kk], acc);
+                const bool tv = (t ? cur1 : cur0) >= 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int pos = p0 + 16 * t + 4 * g + i;
+                    sc[t][i] = (tv && pos < e_j) ? acc[i] * scale2 : -INFINITY;
+                }
+            }
+            if (more)
+                issue_k(cn, pg0, pg1);
+            u32x4 ph, pl;
+            softmax_step<DT, PVS>(sc, m_run, l_run, o, ph, pl);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const u32x4 va = vt_operand<DT>(vt_lane, dt);
+                o[dt] = mfma_bf16(va, ph, o[dt]);
+                if constexpr (PVS)
+                    o[dt] = mfma_bf16(va, pl, o[dt]);
+            }
+            ++q;
+            c = cn;
+            if (!more)
+                break;
         }
     }
 
@@ -300,7 +369,7 @@ decode_mfma_kernel(PartialArgs a)
             }
         }
     } else {
-        __syncthreads();                       // every wave is done with its V tile
+        __syncthreads();                       // every wave is done with its V tiles
         float *cmb_o = (float *)smem;
         if (g == 0) {
             cmb_m[w][j] = m_run;
@@ -344,16 +413,16 @@ template <int D, int KVT, bool PVS, int RW, int NT>
 __global__ void __launch_bounds__(RW * 64)
 multirow_mfma_kernel(PartialArgs a, int row_blocks)
 {
-    constexpr int KK = D / 32, DT = D / 16, UPR = D / 8;
-    constexpr int NTHR = RW * 64;
-    constexpr int UNITS = kChunk * UPR;                 // 8-element units per tile
-    constexpr int UPT = (UNITS + NTHR - 1) / NTHR;      // units per thread
-    constexpr int KRS = 2 * D;                          // K tile row stride (bytes)
-    constexpr int VRS = 2 * D + 16;                     // V tile row stride (bytes)
-    constexpr int SWZ = (UPR < 16 ? UPR : 16) - 1;      // XOR mask on the 16-byte unit
-    constexpr int R = RW * NT * 16;                     // rows per workgroup
-    __shared__ __attribute__((aligned(16))) uint8_t k_lds[kChunk * KRS];
-    __shared__ __attribute__((aligned(16))) uint8_t v_lds[kChunk * VRS];
+    constexpr int KK = D / 32, DT = D / 16;
+    constexpr bool BF = KVT == NBX_BF16;
+    constexpr int ESZ = BF ? 2 : 1;
+    constexpr int KBYTES = kChunk * 2 * D;     // K chunk as bf16: [tile][KK][16 rows][64 B]
+    constexpr int VBYTES = kChunk * 2 * D;     // V chunk as bf16: [tile][DT][16 rows][32 B]
+    constexpr int BUF = KBYTES + VBYTES;
+    constexpr int NI = 2 * KK + DT;            // 1 KB (bf16) loads per chunk: K then V
+    constexpr int MYI = (NI + RW - 1) / RW;    // upper bound of one wave's share
+    constexpr int R = RW * NT * 16;            // rows per workgroup
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF];
 
     const uint32_t id = xcd_contiguous_id(blockIdx.x, gridDim.x);
     const int rb = (int)(id % (uint32_t)row_blocks);
@@ -361,7 +430,8 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
     const int s = rest % a.n_split;
     const int bg = rest / a.n_split;
     const int b = bg / a.kv_heads, gk = bg % a.kv_heads;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, uniform
     const int g = lane >> 4, j = lane & 15;
     const int M = a.rows_per_kv;
     const int row_lo = rb * R, row_hi = min(M, row_lo + R);
@@ -415,52 +485,92 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
             o[n][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
-    u32x4 kr[UPT], vr[UPT];
-    bool tv_next[2] = {false, false};
-    auto gload = [&](int c) {
+    const int64_t k_head = (int64_t)gk * a.k_stride_head;
+    const int64_t v_head = (int64_t)gk * a.v_stride_head;
+    const int kst_b = (int)(a.k_stride_token * ESZ), vst_b = (int)(a.v_stride_token * ESZ);
+    // fixed per-lane byte offsets inside a tile of the 64-lane loads
+    const int k_lane = (lane >> 2) * kst_b + (lane & 3) * 8 * ESZ;   // + kk * 32 * ESZ
+    const int v_lane = ((lane & 31) >> 1) * vst_b + ((lane >> 5) * 16 + (lane & 1) * 8) * ESZ;
+    const uint8_t *k_rd = smem + j * 64 + g * 16;                    // + (t*KK + kk) * 1024
+    const uint8_t *vt_lane = smem + KBYTES + (4 * g + (j >> 2)) * 32 + (j & 3) * 8;
+
+    // page ids of the chunks of even / odd 32-chunk batches (lane i: tile i & 1
+    // of chunk 32 batch + i / 2); two registers, so that refreshing the next
+    // batch keeps the ids of chunks still in flight
+    int pg_even = -1, pg_odd = -1;
+    auto page_of = [&](int c, int t) {
+        const int r = ((c >> 5) & 1) ? pg_odd : pg_even;
+        return __builtin_amdgcn_readlane(r, 2 * (c & 31) + t);
+    };
+    auto refresh = [&](int c) {
+        const int v = chunk_pages(a, b, j0, jend, nchunk, c, 1, lane, lead);
+        if ((c >> 5) & 1)
+            pg_odd = v;
+        else
+            pg_even = v;
+    };
+    u32x4 raw16[BF ? MYI : 1];                 // this wave's share of a chunk in flight
+    u32x2 raw8[BF ? 1 : MYI];                  // (fp8: codes, widened when they land)
+
+    // this wave's share of the loads of chunk c: instructions w, w + RW, ...
+    auto issue = [&](int c, uint8_t *buf) {
         const int p0 = j0 + c * kChunk;
-        int64_t kb[2], vb[2];
+        const int page0 = page_of(c, 0), page1 = page_of(c, 1);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int x = 0; x < MYI; ++x) {
+            const int i = w + x * RW;
+            if (i >= NI)
+                break;
+            const bool isk = i < 2 * KK;
+            const int ii = isk ? i : i - 2 * KK;
+            const int t = isk ? ii / KK : ii / (DT / 2);
             const int ts = p0 + 16 * t;
-            const int page = tile_page(a, b, ts, jend, lead);
-            tv_next[t] = page >= 0;
-            const int64_t off = (int64_t)(ts % a.page_tokens);
-            kb[t] = (int64_t)page * a.k_stride_page + (int64_t)gk * a.k_stride_head +
-                    off * a.k_stride_token;
-            vb[t] = (int64_t)page * a.v_stride_page + (int64_t)gk * a.v_stride_head +
-                    off * a.v_stride_token;
-        }
-#pragma unroll
-        for (int i = 0; i < UPT; ++i) {
-            const int u = i * NTHR + (int)threadIdx.x;
-            const int pr = u / UPR, c8 = u % UPR, t = (pr >> 4) & 1;
-            const bool in = u < UNITS && tv_next[t];
-            kr[i] = in ? load8_bf16<KVT>(a.k_data, kb[t] + (pr & 15) * a.k_stride_token + c8 * 8)
-                       : u32x4{0, 0, 0, 0};
-            vr[i] = (in && p0 + pr < jend)
-                        ? load8_bf16<KVT>(a.v_data, vb[t] + (pr & 15) * a.v_stride_token + c8 * 8)
-                        : u32x4{0, 0, 0, 0};
+            const int page = t ? page1 : page0;
+            i32x4 rs;
+            int voff;
+            uint8_t *dst;
+            if (isk) {
+                const int kk = ii % KK;
+                rs = tile_rsrc<ESZ>(a.k_data, a.k_stride_page, k_head, a.k_stride_token,
+                                    a.page_tokens, page, ts, 16);
+                voff = k_lane + kk * 32 * ESZ;
+                dst = buf + (t * KK + kk) * 1024;
+            } else {
+                const int k = ii % (DT / 2);
+                rs = tile_rsrc<ESZ>(a.v_data, a.v_stride_page, v_head, a.v_stride_token,
+                                    a.page_tokens, page, ts, min(16, jend - ts));
+                voff = v_lane + k * 32 * ESZ;
+                dst = buf + KBYTES + t * DT * 512 + k * 1024;
+            }
+            (void)dst;
+            if constexpr (BF)
+                raw16[x] = nbx_buffer_load_b128(rs, voff, 0, 0);
+            else
+                raw8[x] = nbx_buffer_load_b64(rs, voff, 0, 0);
         }
     };
-
-    if (nchunk > 0)
-        gload(0);
-    for (int c = 0; c < nchunk; ++c) {
-        const bool tv[2] = {tv_next[0], tv_next[1]};
+    // this wave's share of chunk c landed in registers: write it to the chunk's
+    // LDS buffer (rows outside a descriptor range were read as zeros)
+    auto land = [&](uint8_t *buf) {
 #pragma unroll
-        for (int i = 0; i < UPT; ++i) {
-            const int u = i * NTHR + (int)threadIdx.x;
-            if (u < UNITS) {
-                const int pr = u / UPR, c8 = u % UPR;
-                *(u32x4 *)(k_lds + pr * KRS + ((c8 ^ (pr & SWZ)) * 16)) = kr[i];
-                *(u32x4 *)(v_lds + pr * VRS + c8 * 16) = vr[i];
-            }
+        for (int x = 0; x < MYI; ++x) {
+            const int i = w + x * RW;
+            if (i >= NI)
+                break;
+            const bool isk = i < 2 * KK;
+            const int ii = isk ? i : i - 2 * KK;
+            const int t = isk ? ii / KK : ii / (DT / 2);
+            uint8_t *dst = isk ? buf + (t * KK + ii % KK) * 1024
+                               : buf + KBYTES + t * DT * 512 + (ii % (DT / 2)) * 1024;
+            if constexpr (BF)
+                *(u32x4 *)(dst + lane * 16) = raw16[x];
+            else
+                *(u32x4 *)(dst + lane * 16) = widen8_e4m3(raw8[x]);
         }
-        __syncthreads();
-        if (c + 1 < nchunk)
-            gload(c + 1);                  // in flight while this chunk is computed
+    };
+    auto compute = [&](int c, int boff) {
         const int p0 = j0 + c * kChunk;
+        const int page0 = page_of(c, 0), page1 = page_of(c, 1);
         f32x4 acc[NT][2];
 #pragma unroll
         for (int n = 0; n < NT; ++n)
@@ -469,9 +579,7 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
-                const int pr = 16 * t + j;
-                const u32x4 ka =
-                    *(const u32x4 *)(k_lds + pr * KRS + (((kk * 4 + g) ^ (pr & SWZ)) * 16));
+                const u32x4 ka = *(const u32x4 *)(k_rd + boff + (t * KK + kk) * 1024);
 #pragma unroll
                 for (int n = 0; n < NT; ++n)
                     acc[n][t] = mfma_bf16(ka, qb[n][kk], acc[n][t]);
@@ -482,17 +590,19 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
             const int e_n = min(jend, n_row[n]);
             float sc[2][4];
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < 2; ++t) {
+                const bool tv = (t ? page1 : page0) >= 0;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int pos = p0 + 16 * t + 4 * g + i;
-                    sc[t][i] = (tv[t] && pos < e_n) ? acc[n][t][i] * scale2 : -INFINITY;
+                    sc[t][i] = (tv && pos < e_n) ? acc[n][t][i] * scale2 : -INFINITY;
                 }
+            }
             softmax_step<DT, PVS>(sc, m_run[n], l_run[n], o[n], ph[n], pl[n]);
         }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            const u32x4 va = lds_vt_operand(v_lds, VRS, dt * 16, lane);
+            const u32x4 va = vt_operand<DT>(vt_lane + boff, dt);
 #pragma unroll
             for (int n = 0; n < NT; ++n) {
                 o[n][dt] = mfma_bf16(va, ph[n], o[n][dt]);
@@ -500,7 +610,32 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
                     o[n][dt] = mfma_bf16(va, pl[n], o[n][dt]);
             }
         }
-        __syncthreads();                   // the tiles are rewritten next iteration
+    };
+
+    // Chunk c + 1 is in registers while chunk c is computed from LDS; after
+    // computing, it lands in the other LDS buffer and chunk c + 2 is issued.
+    // One barrier per chunk: it publishes chunk c and retires buffer (c + 1) & 1.
+    if (nchunk > 0) {
+        refresh(0);
+        issue(0, smem);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        land(smem);
+        if (nchunk > 1)
+            issue(1, smem + BUF);
+        for (int c = 0; c < nchunk; ++c) {
+            const int boff = (c & 1) * BUF;
+            __syncthreads();
+            compute(c, boff);
+            if (c + 1 < nchunk) {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                land(smem + ((c + 1) & 1) * BUF);
+                if (c + 2 < nchunk) {
+                    if (((c + 2) & 31) == 0)
+                        refresh(c + 2);
+                    issue(c + 2, smem + boff);
+                }
+            }
+        }
     }
 
     const float vs = a.v_scale;
@@ -529,7 +664,7 @@ hipError_t launch_kind(const PartialArgs &a, hipStream_t stream)
 {
     const int M = a.rows_per_kv;
     if (M <= 16) {
-        // waves per (split, head): enough to keep each wave's run of chunks short
+        // waves per (split, head): enough that each wave's run of chunks is short
         const int chunks = (a.split_size + kChunk - 1) / kChunk;
         dim3 grid(a.n_split, a.batch * a.kv_heads);
         if (chunks >= 16)
