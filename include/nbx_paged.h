@@ -156,7 +156,8 @@ size_t nbx_paged_decode_workspace_bytes(int64_t rows, int32_t n_split, int32_t h
  *   m_part       device fp32 [rows, n_split]: max_j s_j (natural-log units)
  *   l_part       device fp32 [rows, n_split]: sum_j exp(s_j - m)
  *                where s_j = scale * pool.scale_k * (q . k_j) over the split.
- *                An empty split stores (0, -inf, 0).
+ *                An empty split (no key of the row in it) stores m = -inf and
+ *                l = 0; its o is left unwritten (the merge never reads it).
  *
  * Supported: pool dtype NBX_F32 with any q dtype; NBX_BF16 or NBX_FP8_E4M3
  * pools with NBX_BF16 or NBX_F32 q.
@@ -171,7 +172,8 @@ int nbx_paged_decode_partial(const void *q, int32_t q_dtype, int32_t batch, int3
 /*
  * nbx_paged_decode_merge - fixed-order combine of split partials (nbxtensor
  * attention_wrappers.py, decode_reduce): per row, M = the largest m_s of the
- * non-empty splits (m_s != -inf), w_s = exp(m_s - M), and
+ * non-empty splits (m_s != -inf; the o of an empty split is not read),
+ * w_s = exp(m_s - M), and
  *   out = sum_s w_s o_s / sum_s w_s l_s,
  * summed in ascending s.  A row with no non-empty split is 0.  NaN in a
  * partial propagates to the row.
@@ -179,6 +181,7 @@ int nbx_paged_decode_partial(const void *q, int32_t q_dtype, int32_t batch, int3
  *   o_part, m_part, l_part  as written by nbx_paged_decode_partial.
  *   out          device [rows, head_dim] of out_dtype (NBX_F32 or NBX_BF16,
  *                bf16 rounded to nearest even).
+ *   n_split      at most 4096, else NBX_ERR_UNSUPPORTED.
  */
 int nbx_paged_decode_merge(const float *o_part, const float *m_part, const float *l_part,
                            int64_t rows, int32_t n_split, int32_t head_dim, void *out,

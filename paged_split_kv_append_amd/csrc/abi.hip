@@ -11,6 +11,7 @@
 namespace {
 
 constexpr int kMaxGridYZ = 65535;
+constexpr int kMaxMergeSplits = 4096;   // the merge keeps one weight per split in LDS
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -263,6 +264,8 @@ int nbx_paged_decode_merge(const float *o_part, const float *m_part, const float
         return NBX_ERR_BAD_DTYPE;
     if (rows < 0 || n_split < 1 || !head_dim_ok(head_dim))
         return NBX_ERR_BAD_SHAPE;
+    if (n_split > kMaxMergeSplits)
+        return NBX_ERR_UNSUPPORTED;
     if (!aligned16(o_part) || !aligned16(out) || ((uintptr_t)m_part & 3u) ||
         ((uintptr_t)l_part & 3u))
         return NBX_ERR_BAD_ALIGN;
@@ -287,6 +290,8 @@ int nbx_paged_decode(const void *q, int32_t q_dtype, int32_t batch, int32_t q_he
         return NBX_ERR_NULL_PTR;
     if (out_dtype != NBX_F32 && out_dtype != NBX_BF16)
         return NBX_ERR_BAD_DTYPE;
+    if (n_split > kMaxMergeSplits)
+        return NBX_ERR_UNSUPPORTED;
     if (batch == 0)
         return NBX_OK;
     const int64_t rows = (int64_t)batch * q_heads * q_rows;

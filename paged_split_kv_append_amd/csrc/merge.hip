@@ -3,7 +3,8 @@
 // order so the result does not depend on scheduling).
 //
 // Per row: M = the largest m_s over non-empty splits (m_s = -inf marks an
-// empty one), w_s = exp(m_s - M), out = sum_s w_s o_s / sum_s w_s l_s.
+// empty one, whose o is not read), w_s = exp(m_s - M), out = sum_s w_s o_s /
+// sum_s w_s l_s.
 //
 // One workgroup of 4 waves per row.  The lanes first take the splits 64 at a
 // time to form M, the weights w_s (kept in LDS) and the denominator by a
@@ -79,12 +80,14 @@ merge_kernel(MergeArgs a)
         for (int u = 0; u < 8; ++u) {
             const float w = w_s[s + 4 * u];
 #pragma unroll
-            for (int k = 0; k < E; ++k)
-                acc[k] = fmaf(w, v[u][k], acc[k]);
+            for (int k = 0; k < E; ++k)   // an empty split's o is not defined: skip it
+                acc[k] = w != 0.0f ? fmaf(w, v[u][k], acc[k]) : acc[k];
         }
     }
     for (; s < ns; s += 4) {
         const float w = w_s[s];
+        if (w == 0.0f)
+            continue;
         const float *os = o + (int64_t)s * D;
 #pragma unroll
         for (int k = 0; k < E; ++k)

@@ -50,6 +50,8 @@
 //    Workgroups are ordered row block fastest and mapped so that the row
 //    blocks of one split run on the same XCD and share its L2 (the rows-first
 //    order of TensorFold PR #1219, made XCD-aware).
+#include <atomic>
+
 #include "kernels.h"
 #include "mfma_common.h"
 
@@ -202,8 +204,12 @@ decode_mfma_kernel(PartialArgs a)
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, uniform
     const int g = lane >> 4, j = lane & 15;
-    const int s = blockIdx.x;
-    const int b = blockIdx.y / a.kv_heads, gk = blockIdx.y % a.kv_heads;
+    // (sequence x KV head) is the fastest index: consecutive workgroups go to
+    // different XCDs, so each XCD gets every split of an equal share of heads
+    const int heads = a.batch * a.kv_heads;
+    const int s = (int)(blockIdx.x / (uint32_t)heads);
+    const int bg = (int)(blockIdx.x % (uint32_t)heads);
+    const int b = bg / a.kv_heads, gk = bg % a.kv_heads;
     const int M = a.rows_per_kv;
     const int64_t row_base = ((int64_t)b * a.q_heads + (int64_t)gk * a.group) * a.q_rows;
     const bool lead = threadIdx.x == 0;
@@ -404,6 +410,301 @@ decode_mfma_kernel(PartialArgs a)
                 a.l_part[row * a.n_split + s] = lv;
             }
         }
+    }
+}
+
+// ------------------------------------------------------------------ persistent decode
+
+constexpr int kPersistMaxBatch = 256;      // sequences covered by the lane-register item table
+
+// One wave per work item = (sequence b, split s, KV head g) with keys in the
+// split.  The grid is sized to the waves the GPU can hold; items are numbered
+// on the device from seq_lens (sequence-major, empty splits never numbered)
+// and dealt out evenly: wave w takes items w, w + W', w + 2 W', ... where W'
+// is the smallest wave count that gives every wave the same number of items.
+// Each wave streams the chunks of its items back to back, with the next
+// chunk's loads (and, one chunk ahead of an item boundary, the next item's Q
+// and page ids) in flight while the current chunk is computed, so the cost of
+// starting a wave is paid once, not once per split.  Splits without keys get
+// m = -inf and l = 0; their o is not written.
+template <int D, int KVT, bool PVS, int NB>
+__global__ void __launch_bounds__(64)
+decode_persistent_kernel(PartialArgs a)
+{
+    constexpr int KK = D / 32, DT = D / 16;
+    constexpr bool BF = KVT == NBX_BF16;
+    constexpr int ESZ = BF ? 2 : 1;
+    constexpr int VBYTES = kChunk * 2 * D;
+    __shared__ __attribute__((aligned(16))) uint8_t tile[VBYTES];
+
+    const int lane = threadIdx.x;
+    const int g = lane >> 4, j = lane & 15;
+    const int wv = blockIdx.x, W = gridDim.x;
+    const int M = a.rows_per_kv, S = a.split_size, H = a.kv_heads, NS = a.n_split;
+    const int cap = a.max_pages * a.page_tokens;
+
+    // sequence table, lane l of block t describing b = 64 t + l: clamped
+    // length, splits holding keys, inclusive prefix of item counts
+    int Lr[NB], nsr[NB], incl[NB];
+    int carry = 0;
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+        const int b = 64 * t + lane;
+        int L = 0;
+        if (b < a.batch) {
+            L = a.seq_lens[b];
+            if (L < 0 || L > cap) {
+                if (wv == 0)
+                    flag_error(a.dev_err, NBX_DEVERR_SEQ_RANGE);
+                L = L < 0 ? 0 : cap;
+            }
+            if (wv == 0 && L > NS * S)
+                flag_error(a.dev_err, NBX_DEVERR_SEQ_RANGE);
+        }
+        int nmax = a.causal ? L - a.q_rows + min(M, a.q_rows) : L;
+        nmax = nmax < 0 ? 0 : nmax;
+        const int ns = b < a.batch ? min((nmax + S - 1) / S, NS) : 0;
+        int x = ns * H;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(x, off, 64);
+            if (lane >= off)
+                x += y;
+        }
+        Lr[t] = L;
+        nsr[t] = ns;
+        incl[t] = carry + x;
+        carry = __shfl(incl[t], 63, 64);
+    }
+    const int N = carry;
+    auto lane_val = [&](const int (&arr)[NB], int b) {
+        int v = arr[0];
+#pragma unroll
+        for (int t = 1; t < NB; ++t)
+            v = (b >> 6) == t ? arr[t] : v;
+        return __builtin_amdgcn_readlane(v, b & 63);
+    };
+
+    // splits without keys: m = -inf, l = 0 for their rows
+    {
+        const int per_b = NS * H, pairs = a.batch * per_b;
+        for (int pi = wv; pi < pairs; pi += W) {
+            const int b = pi / per_b, rem = pi - b * per_b, s = rem / H, gk = rem - s * H;
+            if (s >= lane_val(nsr, b) && lane < M) {
+                const int64_t row =
+                    ((int64_t)b * a.q_heads + (int64_t)gk * a.group) * a.q_rows + lane;
+                a.m_part[row * NS + s] = -INFINITY;
+                a.l_part[row * NS + s] = 0.0f;
+            }
+        }
+    }
+    if (N == 0)
+        return;
+    const int k_per = (N + W - 1) / W;
+    const int W_eff = (N + k_per - 1) / k_per;
+    if (wv >= W_eff)
+        return;
+
+    struct Item {
+        int b, gk, s, j0, jend, e_j, nchunk;
+        int64_t row_base;
+    };
+    auto make_item = [&](int k) {
+        Item it;
+        int before = 0;                        // sequences whose items all precede k
+#pragma unroll
+        for (int t = 0; t < NB; ++t)
+            before += __popcll(__ballot(incl[t] <= k));
+        it.b = before;
+        const int excl = lane_val(incl, it.b) - lane_val(nsr, it.b) * H;
+        const int r = k - excl;
+        it.s = r / H;
+        it.gk = r - it.s * H;
+        const int L = lane_val(Lr, it.b);
+        int nmax = a.causal ? L - a.q_rows + min(M, a.q_rows) : L;
+        nmax = nmax < 0 ? 0 : nmax;
+        it.j0 = it.s * S;
+        it.jend = min(it.j0 + S, nmax);
+        it.nchunk = (it.jend - it.j0 + kChunk - 1) / kChunk;
+        int n_j = 0;
+        if (j < M) {
+            n_j = a.causal ? L - a.q_rows + (j % a.q_rows) + 1 : L;
+            n_j = n_j < 0 ? 0 : n_j;
+        }
+        it.e_j = min(it.jend, n_j);
+        it.row_base = ((int64_t)it.b * a.q_heads + (int64_t)it.gk * a.group) * a.q_rows;
+        return it;
+    };
+    auto load_q = [&](const Item &it, u32x4 (&qv)[KK]) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            qv[kk] = j < M ? *(const u32x4 *)((const uint16_t *)a.q + (it.row_base + j) * D +
+                                              kk * 32 + g * 8)
+                           : u32x4{0, 0, 0, 0};
+    };
+    // lane i: page of tile (i & 1) of chunk c0 + i / 2 of the item
+    auto item_pages = [&](const Item &it, int c0) {
+        const int cq = c0 + (lane >> 1);
+        const int ts = it.j0 + cq * kChunk + 16 * (lane & 1);
+        return cq < it.nchunk ? tile_page(a, it.b, ts, it.jend, true) : -1;
+    };
+
+    const int kst_b = (int)(a.k_stride_token * ESZ), vst_b = (int)(a.v_stride_token * ESZ);
+    const int k_lane = j * kst_b + g * 8 * ESZ;                        // + kk * 32 * ESZ
+    const int v_lane = ((lane & 31) >> 1) * vst_b + ((lane >> 5) * 16 + (lane & 1) * 8) * ESZ;
+    const uint8_t *vt_lane = tile + (4 * g + (j >> 2)) * 32 + (j & 3) * 8;
+    const float scale2 = a.scale * a.k_scale * kLog2e;
+    const float vs = a.v_scale;
+
+    u32x4 kr[2][KK], qb[KK];
+    u32x4 vr[BF ? DT : 1];
+    u32x2 vraw[BF ? 1 : DT];
+    auto issue_v = [&](const Item &it, int c, int pg0, int pg1) {
+        const int p0 = it.j0 + c * kChunk;
+        const int64_t v_head = (int64_t)it.gk * a.v_stride_head;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int ts = p0 + 16 * t;
+            const i32x4 rv = tile_rsrc<ESZ>(a.v_data, a.v_stride_page, v_head, a.v_stride_token,
+                                            a.page_tokens, t ? pg1 : pg0, ts, min(16, it.jend - ts));
+#pragma unroll
+            for (int k = 0; k < DT / 2; ++k) {
+                const int i = t * (DT / 2) + k;
+                if constexpr (BF)
+                    vr[i] = nbx_buffer_load_b128(rv, v_lane + k * 64, 0, 0);
+                else
+                    vraw[i] = nbx_buffer_load_b64(rv, v_lane + k * 32, 0, 0);
+            }
+        }
+    };
+    // K rows of the chunk and, with them, the item's Q rows (a few KB that stay
+    // in L2): one register set each, refilled right after the scores are formed
+    auto issue_k = [&](const Item &it, int c, int pg0, int pg1) {
+        load_q(it, qb);
+        const int p0 = it.j0 + c * kChunk;
+        const int64_t k_head = (int64_t)it.gk * a.k_stride_head;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const i32x4 rk = tile_rsrc<ESZ>(a.k_data, a.k_stride_page, k_head, a.k_stride_token,
+                                            a.page_tokens, t ? pg1 : pg0, p0 + 16 * t, 16);
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                kr[t][kk] = buffer_load8_bf16<KVT>(rk, k_lane + kk * 32 * ESZ);
+        }
+    };
+    auto land_v = [&]() {
+#pragma unroll
+        for (int i = 0; i < DT; ++i) {
+            const int t = i / (DT / 2), k = i % (DT / 2);
+            u32x4 v;
+            if constexpr (BF)
+                v = vr[i];
+            else
+                v = widen8_e4m3(vraw[i]);
+            *(u32x4 *)(tile + t * DT * 512 + k * 1024 + lane * 16) = v;
+        }
+    };
+
+    float m_run = -INFINITY, l_run = 0.0f;
+    f32x4 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+        o[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    int i_item = 0;
+    Item cur = make_item(wv);
+    int pg_reg = item_pages(cur, 0), pg_next = -1;
+    Item nxt = cur;
+    bool has_next = false;
+    auto prepare_next = [&]() {
+        const int kn = wv + (i_item + 1) * W_eff;
+        has_next = i_item + 1 < k_per && kn < N;
+        if (has_next) {
+            nxt = make_item(kn);
+            pg_next = item_pages(nxt, 0);
+        }
+    };
+    int c = 0;
+    int pg0 = __builtin_amdgcn_readlane(pg_reg, 0), pg1 = __builtin_amdgcn_readlane(pg_reg, 1);
+    issue_v(cur, 0, pg0, pg1);
+    issue_k(cur, 0, pg0, pg1);
+    if (cur.nchunk == 1)
+        prepare_next();
+
+    for (;;) {
+        // the chunk to compute: (item `ci`, chunk `cc`) whose loads are in flight
+        const Item ci = cur;
+        const int cc = c, cpg0 = pg0, cpg1 = pg1;
+        land_v();                              // DS operations of the wave run in order
+        bool more = true, new_item = false;
+        if (c + 1 < cur.nchunk) {
+            ++c;
+            if ((c & 31) == 0)
+                pg_reg = item_pages(cur, c);
+        } else if (has_next) {
+            cur = nxt;
+            ++i_item;
+            c = 0;
+            pg_reg = pg_next;
+            new_item = true;
+        } else {
+            more = false;
+        }
+        if (more) {
+            pg0 = __builtin_amdgcn_readlane(pg_reg, 2 * (c & 31));
+            pg1 = __builtin_amdgcn_readlane(pg_reg, 2 * (c & 31) + 1);
+            issue_v(cur, c, pg0, pg1);
+        }
+        const int p0 = ci.j0 + cc * kChunk;
+        float sc[2][4];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk)
+                acc = mfma_bf16(kr[t][kk], qb[kk], acc);
+            const bool tv = (t ? cpg1 : cpg0) >= 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int pos = p0 + 16 * t + 4 * g + i;
+                sc[t][i] = (tv && pos < ci.e_j) ? acc[i] * scale2 : -INFINITY;
+            }
+        }
+        if (more) {
+            issue_k(cur, c, pg0, pg1);
+            if (c == cur.nchunk - 1)
+                prepare_next();
+        }
+        u32x4 ph, pl;
+        softmax_step<DT, PVS>(sc, m_run, l_run, o, ph, pl);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            const u32x4 va = vt_operand<DT>(vt_lane, dt);
+            o[dt] = mfma_bf16(va, ph, o[dt]);
+            if constexpr (PVS)
+                o[dt] = mfma_bf16(va, pl, o[dt]);
+        }
+        if (cc == ci.nchunk - 1) {             // item done: store its partial, reset
+            const float lt = xor_sum16_32(l_run);
+            if (j < M) {
+                const int64_t row = ci.row_base + j;
+                float *op = a.o_part + (row * NS + ci.s) * D;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+                    *(f32x4 *)(op + dt * 16 + 4 * g) = o[dt] * vs;
+                if (g == 0) {
+                    a.m_part[row * NS + ci.s] = m_run == -INFINITY ? -INFINITY : m_run * kLn2;
+                    a.l_part[row * NS + ci.s] = lt;
+                }
+            }
+            m_run = -INFINITY;
+            l_run = 0.0f;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+                o[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+        if (!more)
+            break;
     }
 }
 
@@ -659,14 +960,59 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
 
 // ------------------------------------------------------------------ dispatch
 
+// Waves the current device holds at once for the persistent decode kernel
+// (resident workgroups per CU x CUs), cached per device.
+template <int D, int KVT, bool PVS, int NB>
+int persistent_waves()
+{
+    constexpr int kMaxDev = 64;
+    static std::atomic<int> cache[kMaxDev];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return 0;
+    if (dev < kMaxDev) {
+        const int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0)
+            return v;
+    }
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void *>(&decode_persistent_kernel<D, KVT, PVS, NB>), 64,
+            0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    const int v = per_cu * cus;
+    if (dev < kMaxDev)
+        cache[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
 template <int D, int KVT, bool PVS>
 hipError_t launch_kind(const PartialArgs &a, hipStream_t stream)
 {
     const int M = a.rows_per_kv;
+    if (M <= 16 && a.batch <= kPersistMaxBatch) {
+        const int64_t items = (int64_t)a.batch * a.kv_heads * a.n_split;
+        const int waves = a.batch <= 64 ? persistent_waves<D, KVT, PVS, 1>()
+                                        : persistent_waves<D, KVT, PVS, 4>();
+        if (waves <= 0)
+            return hipErrorInvalidConfiguration;
+        const int grid = (int)(items < waves ? items : waves);
+        if (a.batch <= 64)
+            hipLaunchKernelGGL((decode_persistent_kernel<D, KVT, PVS, 1>), dim3(grid), dim3(64),
+                               0, stream, a);
+        else
+            hipLaunchKernelGGL((decode_persistent_kernel<D, KVT, PVS, 4>), dim3(grid), dim3(64),
+                               0, stream, a);
+        return hipGetLastError();
+    }
     if (M <= 16) {
         // waves per (split, head): enough that each wave's run of chunks is short
         const int chunks = (a.split_size + kChunk - 1) / kChunk;
-        dim3 grid(a.n_split, a.batch * a.kv_heads);
+        const int64_t blocks = (int64_t)a.n_split * a.batch * a.kv_heads;
+        if (blocks > 0x7FFFFFFF)
+            return hipErrorInvalidConfiguration;
+        dim3 grid((unsigned)blocks);
         if (chunks >= 16)
             hipLaunchKernelGGL((decode_mfma_kernel<D, KVT, PVS, 4>), grid, dim3(256), 0, stream, a);
         else if (chunks >= 4)

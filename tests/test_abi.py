@@ -121,6 +121,7 @@ def test_merge_validation(lib):
     assert m(dt=2) == -2
     assert m(D=100) == -3
     assert m(ns=0) == -3
+    assert m(ns=4097) == -6
     assert m(out=FAKE + 2) == -4
 
 
