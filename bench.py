@@ -40,6 +40,155 @@ WORKLOAD_TEXT = {
 }
 
 
+class HipEvent:
+    """A HIP event recorded with a device-scope release, so recording it costs no
+    system-scope cache write-back between the kernels it brackets."""
+    _hip = None
+    RELEASE_TO_DEVICE = 0x40000000
+
+    def __init__(self):
+        import ctypes
+        if HipEvent._hip is None:
+            import torch  # noqa: F401  (loads the HIP runtime)
+            HipEvent._hip = ctypes.CDLL("libamdhip64.so")
+            HipEvent._hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            HipEvent._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                          ctypes.c_void_p, ctypes.c_void_p]
+        self._ct = ctypes
+        self.ev = ctypes.c_void_p()
+        st = HipEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.ev),
+                                                   ctypes.c_uint(self.RELEASE_TO_DEVICE))
+        if st != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {st}")
+
+    def record(self, stream_ptr: int):
+        st = HipEvent._hip.hipEventRecord(self.ev, self._ct.c_void_p(stream_ptr))
+        if st != 0:
+            raise RuntimeError(f"hipEventRecord failed: {st}")
+
+    def elapsed_ms(self, end: "HipEvent") -> float:
+        ms = self._ct.c_float()
+        st = HipEvent._hip.hipEventElapsedTime(self._ct.byref(ms), self.ev, end.ev)
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {st}")
+        return float(ms.value)
+
+    def __del__(self):
+        if HipEvent._hip is not None and self.ev:
+            HipEvent._hip.hipEventDestroy(self.ev)
+
+
+# Kernel sources whose text decides the split partial's memory traffic.
+PARTIAL_SOURCES = ("paged_split_kv_append_amd/csrc/partial_mfma.hip",
+                   "paged_split_kv_append_amd/csrc/mfma_common.h",
+                   "paged_split_kv_append_amd/csrc/device_common.h",
+                   "paged_split_kv_append_amd/csrc/partial_valu.hip")
+
+
+def partial_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in PARTIAL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(workload: int) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_split_partial_workload{workload}.txt")
+
+
+def load_traffic(workload: int):
+    """HBM bytes per launch of the split partial from the committed counter summary,
+    or None when there is none or the kernel sources changed since it was taken."""
+    path = traffic_file(workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("partial_source_sha256_16") != partial_source_hash():
+        return None
+    return int(kv["traffic_bytes_per_launch"])
+
+
+def _counter_means(d: str, name_part: str):
+    """{kernel name: (dispatches, mean counter value)} from a rocprofv3 --pmc csv."""
+    import csv
+    import glob
+    out = {}
+    for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if name_part in r["Kernel_Name"]:
+                    key = (r["Kernel_Name"], r["Grid_Size"])
+                    n, t = out.get(key, (0, 0.0))
+                    out[key] = (n + 1, t + float(r["Counter_Value"]))
+    return {k: (n, t / n) for k, (n, t) in out.items()}
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, copy_mib: int, workload: int):
+    """Per-launch HBM traffic of the split partial from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the same
+    counter reads for a plain device copy of copy_mib MiB (reads and writes
+    copy_mib MiB)."""
+    copy_kib = copy_mib * 1024.0
+
+    def one(d, counter):
+        copies = [v for (name, grid), v in _counter_means(d, "copyBuffer").items()
+                  if v[1] > copy_kib / 8]
+        if not copies:
+            raise SystemExit(f"no copy kernel of {copy_mib} MiB in {d}")
+        factor = copy_kib / copies[0][1]
+        parts = [(name, v) for (name, grid), v in _counter_means(d, "nbx::").items()
+                 if "persistent" in name or "mfma" in name or "valu" in name]
+        return factor, copies[0][1], parts
+
+    ff, fcopy, fparts = one(fetch_dir, "FETCH_SIZE")
+    wf, wcopy, wparts = one(write_dir, "WRITE_SIZE")
+    fk = max(fparts, key=lambda t: t[1][1])
+    wk = [v for n, v in wparts if n == fk[0]][0]
+    fetch_b = fk[1][1] * ff * 1024
+    write_b = wk[1] * wf * 1024
+    lines = [
+        f"# split partial HBM traffic, workload {workload}",
+        f"kernel: {fk[0]}",
+        f"dispatches_counted: {fk[1][0]}",
+        f"copy_reference_mib: {copy_mib}",
+        f"fetch_size_copy_kib: {fcopy:.2f}",
+        f"fetch_factor: {ff:.5f}",
+        f"write_size_copy_kib: {wcopy:.2f}",
+        f"write_factor: {wf:.5f}",
+        f"fetch_size_kib_per_dispatch: {fk[1][1]:.2f}",
+        f"write_size_kib_per_dispatch: {wk[1]:.2f}",
+        f"fetch_bytes_per_launch: {int(fetch_b)}",
+        f"write_bytes_per_launch: {int(write_b)}",
+        f"traffic_bytes_per_launch: {int(fetch_b + write_b)}",
+        f"partial_source_sha256_16: {partial_source_hash()}",
+    ]
+    return "\n".join(lines)
+
+
+def summarize_trace(trace_dir: str):
+    """The kernel-stats table of a rocprofv3 --kernel-trace --stats run, in us."""
+    import csv
+    import glob
+    fn = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
+    rows = list(csv.DictReader(open(fn)))
+    out = [f"{'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'pct':>6}  kernel"]
+    for r in rows:
+        name = r["Name"]
+        if len(name) > 90:
+            name = name[:87] + "..."
+        out.append(f"{int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>9.2f} "
+                   f"{float(r['MinNs']) / 1e3:>9.2f} {float(r['MaxNs']) / 1e3:>9.2f} "
+                   f"{float(r['Percentage']):>6.2f}  {name}")
+    return "\n".join(out)
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -98,7 +247,21 @@ def main():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush-mib", type=int, default=1024)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (a known-size "
+                         "reference for the profiler's byte counters)")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print the kernel table of a rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the split partial's traffic from FETCH_SIZE / WRITE_SIZE runs "
+                         "made with --copy-mib")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return
+    if args.summarize_counters:
+        print(summarize_counters(*args.summarize_counters, args.copy_mib or 256, args.workload))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -139,50 +302,58 @@ def main():
     l_part = torch.empty(rows, n_split, device=dev)
     out = torch.empty(case.batch, case.q_heads, case.q_rows, D, device=dev)
     flush = torch.ones(args.flush_mib * (1 << 18), device=dev) if args.flush_mib else None
-    stream = torch.cuda.current_stream()
+    stream_ptr = torch.cuda.current_stream().cuda_stream
 
-    def step(ev=None):
+    def step(part_ev=None):
         if has_append:
             nb.nbx_paged_kv_append(new_k, new_v, kp, vp, slots, dev_err=err)
-        if ev is not None:
-            ev[0].record(stream)
+        if part_ev is not None:
+            part_ev[0].record(stream_ptr)
         nb.nbx_paged_decode_partial(q, kp, vp, bt, lens, case.softmax_scale, split, n_split,
                                     o_part, m_part, l_part, causal=case.causal, dev_err=err)
-        if ev is not None:
-            ev[1].record(stream)
+        if part_ev is not None:
+            part_ev[1].record(stream_ptr)
         nb.nbx_paged_decode_merge(o_part, m_part, l_part, out)
 
+    def flush_caches():
+        if flush is not None:
+            flush.sum()                      # read 1 GiB: evicts K/V from L2 and MALL
+
+    if args.copy_mib:
+        src = torch.ones(args.copy_mib * (1 << 18), device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
+        flush_caches()
         step()
     torch.cuda.synchronize()
     if int(err.item()) != 0:
         raise RuntimeError(f"device error flags {int(err.item())}")
 
     K = args.steps
-    ev_step = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(K)]
-    ev_part = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(K)]
+    # Pass 1: whole steps, events only at the step boundaries.
+    ev_step = [(HipEvent(), HipEvent()) for _ in range(K)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     for i in range(K):
-        if flush is not None:
-            flush.sum()                      # read 1 GiB: evicts K/V from L2 and MALL
-        ev_step[i][0].record(stream)
-        step(ev_part[i])
-        ev_step[i][1].record(stream)
+        flush_caches()
+        ev_step[i][0].record(stream_ptr)
+        step()
+        ev_step[i][1].record(stream_ptr)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
-    step_ms = np.array([a.elapsed_time(b) for a, b in ev_step])
-    part_ms = np.array([a.elapsed_time(b) for a, b in ev_part])
-
-    # warm steps (no flush) for context
+    step_ms = np.array([a.elapsed_ms(b) for a, b in ev_step])
+    # Pass 2: the same steps with events bracketing the split partial alone.
+    ev_part = [(HipEvent(), HipEvent()) for _ in range(K)]
     for i in range(K):
-        ev_step[i][0].record(stream)
-        step()
-        ev_step[i][1].record(stream)
+        flush_caches()
+        step(ev_part[i])
     torch.cuda.synchronize()
-    warm_ms = np.array([a.elapsed_time(b) for a, b in ev_step])
+    part_ms = np.array([a.elapsed_ms(b) for a, b in ev_part])
+    if int(err.item()) != 0:
+        raise RuntimeError(f"device error flags {int(err.item())}")
 
     kv = case.kv_bytes()
     t_step = float(step_ms.mean()) * 1e-3
@@ -209,11 +380,10 @@ def main():
         "us_per_step_p10_p90": [round(float(np.percentile(step_ms, 10)) * 1e3, 2),
                                 round(float(np.percentile(step_ms, 90)) * 1e3, 2)],
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "warm_us_per_step": round(float(warm_ms.mean()) * 1e3, 2),
         "wall_s_timed_loop": round(wall, 4),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(args.workload),
             "kernel": "split partial", "us_per_launch": round(t_part * 1e6, 2),
         },
     }
