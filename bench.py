@@ -94,14 +94,15 @@ def partial_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_file(workload: int) -> str:
-    return os.path.join(ROOT, "profiles", f"traffic_split_partial_workload{workload}.txt")
+def traffic_file(workload: int, fused: bool) -> str:
+    tag = "step" if fused else "split_partial"
+    return os.path.join(ROOT, "profiles", f"traffic_{tag}_workload{workload}.txt")
 
 
-def load_traffic(workload: int):
+def load_traffic(workload: int, fused: bool):
     """HBM bytes per launch of the split partial from the committed counter summary,
     or None when there is none or the kernel sources changed since it was taken."""
-    path = traffic_file(workload)
+    path = traffic_file(workload, fused)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -247,6 +248,9 @@ def main():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush-mib", type=int, default=1024)
+    ap.add_argument("--unfused", action="store_true",
+                    help="time the append, partial and merge as three calls instead of the "
+                         "single-launch step")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size "
                          "reference for the profiler's byte counters)")
@@ -304,7 +308,29 @@ def main():
     flush = torch.ones(args.flush_mib * (1 << 18), device=dev) if args.flush_mib else None
     stream_ptr = torch.cuda.current_stream().cuda_stream
 
+    fused = not args.unfused
+    if fused:
+        ws = torch.empty(nb.nbx_paged_decode_workspace_bytes(rows, n_split, D), dtype=torch.uint8,
+                         device=dev)
+        o_ws, m_ws, l_ws = nb.workspace_partials(ws, rows, n_split, D)
+        nk4 = new_k.unsqueeze(1) if has_append else None
+        nv4 = new_v.unsqueeze(1) if has_append else None
+
     def step(part_ev=None):
+        if fused:
+            # the append runs inside the split-partial launch (one kernel), then the merge
+            if part_ev is None:
+                nb.nbx_paged_decode_step(q, kp, vp, bt, lens, case.softmax_scale, split, n_split,
+                                         ws, out, new_k=nk4, new_v=nv4, causal=case.causal,
+                                         dev_err=err)
+            else:
+                part_ev[0].record(stream_ptr)
+                nb.nbx_paged_decode_step(q, kp, vp, bt, lens, case.softmax_scale, split, n_split,
+                                         ws, None, new_k=nk4, new_v=nv4, causal=case.causal,
+                                         dev_err=err)
+                part_ev[1].record(stream_ptr)
+                nb.nbx_paged_decode_merge(o_ws, m_ws, l_ws, out)
+            return
         if has_append:
             nb.nbx_paged_kv_append(new_k, new_v, kp, vp, slots, dev_err=err)
         if part_ev is not None:
@@ -374,6 +400,10 @@ def main():
         "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8_e4m3"}[case.kv_dtype],
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.workload], "kv_bytes": kv,
+                   "path": ("nbx_paged_decode_step: one launch for append + partials, then "
+                            "the merge" if fused else
+                            "nbx_paged_kv_append, nbx_paged_decode_partial, "
+                            "nbx_paged_decode_merge"),
                    "n_split": n_split, "split_size": split, "rows": rows,
                    "seed": args.seed if args.seed is not None else args.workload},
         "us_per_step": round(float(step_ms.mean()) * 1e3, 2),
@@ -383,8 +413,11 @@ def main():
         "wall_s_timed_loop": round(wall, 4),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(args.workload),
-            "kernel": "split partial", "us_per_launch": round(t_part * 1e6, 2),
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": load_traffic(args.workload, fused),
+            "kernel": ("split partial with the append fused in" if fused and has_append
+                       else "split partial"),
+            "us_per_launch": round(t_part * 1e6, 2),
         },
     }
     if case.kv_dtype in MFMA_PEAK_TFLOPS and case.q_rows > 1:

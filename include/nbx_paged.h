@@ -200,6 +200,51 @@ int nbx_paged_decode(const void *q, int32_t q_dtype, int32_t batch, int32_t q_he
                      void *workspace, size_t workspace_bytes, void *out, int32_t out_dtype,
                      int32_t *dev_err, hipStream_t stream);
 
+/*
+ * nbx_paged_decode_step - one decode step: append the new tokens of every
+ * sequence at its last positions, then partial and merge (nbxtensor
+ * paged_decode_attn.py, paged_kv_append_step_kernel: the step's position is
+ * found on the device from the sequence length and its page from the block
+ * table, so the call's arguments do not change from step to step; then
+ * paged_decode_attn_split_kernel and nbxtensor attention_wrappers.py,
+ * decode_reduce).  Here seq_lens already count the new positions (the pages
+ * advance the length in a separate launch after the append).
+ *
+ * Equivalent to nbx_paged_kv_append with slot_mapping[b * n_new + i] = the
+ * slot of position seq_lens[b] - n_new + i of sequence b (read from the block
+ * table on the device), followed by nbx_paged_decode with the same arguments.
+ * seq_lens count the new positions.  Where the shape allows (bf16 Q, bf16 or
+ * fp8 pool, at most 16 rows per KV head, batch <= 256) the whole step is one
+ * kernel launch; otherwise the append, partial and merge kernels run in turn
+ * on `stream`.
+ *
+ *   new_k, new_v   device, [batch, n_new, kv_heads, head_dim] contiguous, of
+ *                  new_dtype (NBX_F32 or NBX_BF16); stored with the
+ *                  conversions of nbx_paged_kv_append.  Ignored if n_new == 0.
+ *   n_new          new positions per sequence (>= 0).  A sequence shorter
+ *                  than n_new sets NBX_DEVERR_SEQ_RANGE and its tokens that
+ *                  would land before position 0 are skipped; a block-table
+ *                  entry outside the pool sets NBX_DEVERR_PAGE_RANGE and that
+ *                  token is skipped.  The slots of the new positions must not
+ *                  be read by another sequence of the same call.
+ *   workspace      as for nbx_paged_decode.  It holds the partials afterwards:
+ *                  o at offset 0, m at round256(rows * n_split * head_dim * 4),
+ *                  l after m at round256(rows * n_split * 4), the layouts of
+ *                  nbx_paged_decode_partial (round256 = next multiple of 256).
+ *   out            may be null: the step then stops after the partials (for a
+ *                  caller that merges later, e.g. after gathering the partials
+ *                  of other position ranges) and out_dtype is ignored.
+ * Other arguments, errors and results as for nbx_paged_decode.
+ */
+int nbx_paged_decode_step(const void *q, int32_t q_dtype, int32_t batch, int32_t q_heads,
+                          int32_t q_rows, int32_t causal, const void *new_k, const void *new_v,
+                          int32_t new_dtype, int32_t n_new, const nbx_kv_pool *k_pool,
+                          const nbx_kv_pool *v_pool, const int32_t *block_table,
+                          int32_t max_pages, const int32_t *seq_lens, float scale,
+                          int32_t split_size, int32_t n_split, void *workspace,
+                          size_t workspace_bytes, void *out, int32_t out_dtype, int32_t *dev_err,
+                          hipStream_t stream);
+
 /* nbx_status_str - static message text for a status code (never null). */
 const char *nbx_status_str(int status);
 

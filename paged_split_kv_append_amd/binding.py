@@ -77,6 +77,10 @@ def load_library():
             lib.nbx_paged_decode.argtypes = [P, I32, I32, I32, I32, I32, PP, PP, P, I32, P, F, I32,
                                              I32, P, SZ, P, I32, P, P]
             lib.nbx_paged_decode.restype = ctypes.c_int
+            lib.nbx_paged_decode_step.argtypes = [P, I32, I32, I32, I32, I32, P, P, I32, I32, PP,
+                                                  PP, P, I32, P, F, I32, I32, P, ctypes.c_size_t,
+                                                  P, I32, P, P]
+            lib.nbx_paged_decode_step.restype = ctypes.c_int
             lib.nbx_status_str.argtypes = [ctypes.c_int]
             lib.nbx_status_str.restype = ctypes.c_char_p
             lib.nbx_version.restype = ctypes.c_int
@@ -233,3 +237,47 @@ def nbx_paged_decode(q, k_pool: KVPool, v_pool: KVPool, block_table, seq_lens, s
         int(n_split), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
         _dtype_code(out), _ptr(dev_err), _stream(stream))
     _check(st, "nbx_paged_decode")
+
+
+def nbx_paged_decode_step(q, k_pool: KVPool, v_pool: KVPool, block_table, seq_lens, scale: float,
+                          split_size: int, n_split: int, workspace, out, new_k=None, new_v=None,
+                          causal: bool = False, dev_err=None, stream=None):
+    """One decode step: new_k / new_v [batch, n_new, kv_heads, head_dim] (fp32 or bf16,
+    contiguous) written at each sequence's last n_new positions, then partial and merge.
+    ``seq_lens`` count the new positions; ``workspace`` as for nbx_paged_decode.  With
+    ``out=None`` the step stops after the partials, which stay in the workspace."""
+    kd, vd = _decode_common(q, k_pool, v_pool, block_table, seq_lens)
+    B, Hq, W, D = q.shape
+    if out is not None and (out.numel() != B * Hq * W * D or not out.is_contiguous()):
+        raise ValueError("out must be contiguous [batch, q_heads, q_rows, head_dim]")
+    n_new, new_dt = 0, 0
+    if new_k is not None:
+        if new_v is None or new_k.shape != new_v.shape or new_k.dtype != new_v.dtype:
+            raise ValueError("new_k and new_v must match")
+        if new_k.dim() != 4 or new_k.shape[0] != B or new_k.shape[2] != k_pool.data.shape[1] \
+                or new_k.shape[3] != D or not (new_k.is_contiguous() and new_v.is_contiguous()):
+            raise ValueError("new_k / new_v must be contiguous [batch, n_new, kv_heads, head_dim]")
+        n_new, new_dt = new_k.shape[1], _dtype_code(new_k)
+    st = load_library().nbx_paged_decode_step(
+        _ptr(q), _dtype_code(q), B, Hq, W, int(bool(causal)), _ptr(new_k), _ptr(new_v), new_dt,
+        n_new, ctypes.byref(kd), ctypes.byref(vd), _ptr(block_table), block_table.shape[1],
+        _ptr(seq_lens), float(scale), int(split_size), int(n_split), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out),
+        _dtype_code(out) if out is not None else 0, _ptr(dev_err), _stream(stream))
+    _check(st, "nbx_paged_decode_step")
+
+
+def workspace_partials(workspace, rows: int, n_split: int, head_dim: int):
+    """Views (o [rows, n_split, D], m, l [rows, n_split]) of the partials a step or a
+    one-call decode leaves in ``workspace`` (fp32, each part 256-byte aligned)."""
+    r256 = lambda x: (x + 255) // 256 * 256
+    o_b = rows * n_split * head_dim * 4
+    ml_b = rows * n_split * 4
+    need = r256(o_b) + 2 * r256(ml_b)
+    if workspace.dtype != torch.uint8 or workspace.numel() < need:
+        raise ValueError("workspace too small for the partials")
+    o = workspace[:o_b].view(torch.float32).view(rows, n_split, head_dim)
+    m = workspace[r256(o_b):r256(o_b) + ml_b].view(torch.float32).view(rows, n_split)
+    off = r256(o_b) + r256(ml_b)
+    l = workspace[off:off + ml_b].view(torch.float32).view(rows, n_split)
+    return o, m, l

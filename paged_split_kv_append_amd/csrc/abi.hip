@@ -196,24 +196,14 @@ static int validate_partial(const void *q, int32_t q_dtype, int32_t batch, int32
     return NBX_OK;
 }
 
-int nbx_paged_decode_partial(const void *q, int32_t q_dtype, int32_t batch, int32_t q_heads,
-                             int32_t q_rows, int32_t causal, const nbx_kv_pool *k_pool,
-                             const nbx_kv_pool *v_pool, const int32_t *block_table,
-                             int32_t max_pages, const int32_t *seq_lens, float scale,
-                             int32_t split_size, int32_t n_split, float *o_part, float *m_part,
-                             float *l_part, int32_t *dev_err, hipStream_t stream)
+static nbx::PartialArgs partial_args(const void *q, int32_t q_dtype, int32_t batch,
+                                     int32_t q_heads, int32_t q_rows, int32_t causal,
+                                     const nbx_kv_pool *k_pool, const nbx_kv_pool *v_pool,
+                                     const int32_t *block_table, int32_t max_pages,
+                                     const int32_t *seq_lens, float scale, int32_t split_size,
+                                     int32_t n_split, float *o_part, float *m_part, float *l_part,
+                                     int32_t *dev_err)
 {
-    int st = validate_partial(q, q_dtype, batch, q_heads, q_rows, causal, k_pool, v_pool,
-                              block_table, max_pages, seq_lens, scale, split_size, n_split);
-    if (st != NBX_OK)
-        return st;
-    if (!o_part || !m_part || !l_part)
-        return NBX_ERR_NULL_PTR;
-    if (!aligned16(o_part) || ((uintptr_t)m_part & 3u) || ((uintptr_t)l_part & 3u))
-        return NBX_ERR_BAD_ALIGN;
-    if (batch == 0)
-        return NBX_OK;
-
     nbx::PartialArgs a{};
     a.q = q;
     a.q_dtype = q_dtype;
@@ -248,10 +238,46 @@ int nbx_paged_decode_partial(const void *q, int32_t q_dtype, int32_t batch, int3
     a.m_part = m_part;
     a.l_part = l_part;
     a.dev_err = dev_err;
+    return a;
+}
+
+// matrix cores for 16/8-bit pools read with bf16 Q; the vector-ALU kernel for
+// fp32 pools and fp32 Q
+static bool uses_mfma(const nbx::PartialArgs &a)
+{
+    return a.q_dtype == NBX_BF16 && (a.kv_dtype == NBX_BF16 || a.kv_dtype == NBX_FP8_E4M3);
+}
+
+static hipError_t launch_partial(const nbx::PartialArgs &a, hipStream_t stream)
+{
+    return uses_mfma(a) ? nbx::launch_partial_mfma(a, stream) : nbx::launch_partial_valu(a, stream);
+}
+
+int nbx_paged_decode_partial(const void *q, int32_t q_dtype, int32_t batch, int32_t q_heads,
+                             int32_t q_rows, int32_t causal, const nbx_kv_pool *k_pool,
+                             const nbx_kv_pool *v_pool, const int32_t *block_table,
+                             int32_t max_pages, const int32_t *seq_lens, float scale,
+                             int32_t split_size, int32_t n_split, float *o_part, float *m_part,
+                             float *l_part, int32_t *dev_err, hipStream_t stream)
+{
+    int st = validate_partial(q, q_dtype, batch, q_heads, q_rows, causal, k_pool, v_pool,
+                              block_table, max_pages, seq_lens, scale, split_size, n_split);
+    if (st != NBX_OK)
+        return st;
+    if (!o_part || !m_part || !l_part)
+        return NBX_ERR_NULL_PTR;
+    if (!aligned16(o_part) || ((uintptr_t)m_part & 3u) || ((uintptr_t)l_part & 3u))
+        return NBX_ERR_BAD_ALIGN;
+    if (batch == 0)
+        return NBX_OK;
+
+    const nbx::PartialArgs a =
+        partial_args(q, q_dtype, batch, q_heads, q_rows, causal, k_pool, v_pool, block_table,
+                     max_pages, seq_lens, scale, split_size, n_split, o_part, m_part, l_part,
+                     dev_err);
     // matrix cores for 16/8-bit pools read with bf16 Q; the vector-ALU kernel
     // for fp32 pools and fp32 Q
-    const bool mfma = q_dtype == NBX_BF16 && (a.kv_dtype == NBX_BF16 || a.kv_dtype == NBX_FP8_E4M3);
-    return to_status(mfma ? nbx::launch_partial_mfma(a, stream) : nbx::launch_partial_valu(a, stream));
+    return to_status(launch_partial(a, stream));
 }
 
 int nbx_paged_decode_merge(const float *o_part, const float *m_part, const float *l_part,
@@ -310,6 +336,104 @@ int nbx_paged_decode(const void *q, int32_t q_dtype, int32_t batch, int32_t q_he
         return st;
     return nbx_paged_decode_merge(o_part, m_part, l_part, rows, n_split, D, out, out_dtype,
                                   stream);
+}
+
+int nbx_paged_decode_step(const void *q, int32_t q_dtype, int32_t batch, int32_t q_heads,
+                          int32_t q_rows, int32_t causal, const void *new_k, const void *new_v,
+                          int32_t new_dtype, int32_t n_new, const nbx_kv_pool *k_pool,
+                          const nbx_kv_pool *v_pool, const int32_t *block_table,
+                          int32_t max_pages, const int32_t *seq_lens, float scale,
+                          int32_t split_size, int32_t n_split, void *workspace,
+                          size_t workspace_bytes, void *out, int32_t out_dtype, int32_t *dev_err,
+                          hipStream_t stream)
+{
+    int st = validate_partial(q, q_dtype, batch, q_heads, q_rows, causal, k_pool, v_pool,
+                              block_table, max_pages, seq_lens, scale, split_size, n_split);
+    if (st != NBX_OK)
+        return st;
+    if (out && out_dtype != NBX_F32 && out_dtype != NBX_BF16)
+        return NBX_ERR_BAD_DTYPE;
+    if (n_new < 0)
+        return NBX_ERR_BAD_SHAPE;
+    if (n_new > 0) {
+        if (!new_k || !new_v)
+            return NBX_ERR_NULL_PTR;
+        if (new_dtype != NBX_F32 && new_dtype != NBX_BF16)
+            return NBX_ERR_BAD_DTYPE;
+        if (!aligned16(new_k) || !aligned16(new_v))
+            return NBX_ERR_BAD_ALIGN;
+        if ((int64_t)batch * n_new * k_pool->kv_heads * (k_pool->head_dim / 8) >
+            (int64_t)INT32_MAX * 256)
+            return NBX_ERR_BAD_SHAPE;
+    }
+    if (n_split > kMaxMergeSplits)
+        return NBX_ERR_UNSUPPORTED;
+    if (out && !aligned16(out))
+        return NBX_ERR_BAD_ALIGN;
+    if (batch == 0)
+        return NBX_OK;
+    const int64_t rows = (int64_t)batch * q_heads * q_rows;
+    const int32_t D = k_pool->head_dim;
+    const size_t need = nbx_paged_decode_workspace_bytes(rows, n_split, D);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
+        return NBX_ERR_WORKSPACE;
+    char *ws = (char *)workspace;
+    float *o_part = (float *)ws;
+    float *m_part = (float *)(ws + round256((size_t)rows * n_split * D * sizeof(float)));
+    float *l_part = (float *)((char *)m_part + round256((size_t)rows * n_split * sizeof(float)));
+    nbx::PartialArgs a =
+        partial_args(q, q_dtype, batch, q_heads, q_rows, causal, k_pool, v_pool, block_table,
+                     max_pages, seq_lens, scale, split_size, n_split, o_part, m_part, l_part,
+                     dev_err);
+    hipError_t e = hipSuccess;
+    if (n_new > 0 && uses_mfma(a) && nbx::partial_mfma_is_persistent(a)) {
+        // one launch: the wave owning each new position writes it, then reads it
+        a.new_k = new_k;
+        a.new_v = new_v;
+        a.new_dtype = new_dtype;
+        a.n_new = n_new;
+        e = nbx::launch_partial_mfma(a, stream);
+    } else {
+        if (n_new > 0) {
+            nbx::AppendArgs ap{};
+            ap.new_k = new_k;
+            ap.new_v = new_v;
+            ap.src_dtype = new_dtype;
+            ap.dst_dtype = k_pool->dtype;
+            ap.n_tok = (int64_t)batch * n_new;
+            ap.new_stride_tok = (int64_t)k_pool->kv_heads * D;
+            ap.new_stride_head = D;
+            ap.kv_heads = k_pool->kv_heads;
+            ap.head_dim = D;
+            ap.num_pages = k_pool->num_pages;
+            ap.page_tokens = k_pool->page_tokens;
+            ap.k_data = k_pool->data;
+            ap.k_stride_page = k_pool->stride_page;
+            ap.k_stride_head = k_pool->stride_head;
+            ap.k_stride_token = k_pool->stride_token;
+            ap.v_data = v_pool->data;
+            ap.v_stride_page = v_pool->stride_page;
+            ap.v_stride_head = v_pool->stride_head;
+            ap.v_stride_token = v_pool->stride_token;
+            ap.k_scale = k_pool->scale;
+            ap.v_scale = v_pool->scale;
+            ap.slot_mapping = nullptr;
+            ap.dev_err = dev_err;
+            ap.seq_lens = seq_lens;
+            ap.block_table = block_table;
+            ap.max_pages = max_pages;
+            ap.n_new = n_new;
+            e = nbx::launch_append(ap, stream);
+        }
+        if (e == hipSuccess)
+            e = launch_partial(a, stream);
+    }
+    if (e != hipSuccess)
+        return NBX_ERR_LAUNCH;
+    if (!out)
+        return NBX_OK;                         // partials only, left in the workspace
+    nbx::MergeArgs m{o_part, m_part, l_part, rows, n_split, D, out, out_dtype};
+    return to_status(nbx::launch_merge(m, stream));
 }
 
 }  // extern "C"

@@ -3,6 +3,9 @@
 // slot per new token, slot = page * page_tokens + row, the values cast to the
 // pool's dtype on store).
 //
+// Tail mode (no slot mapping): the n_new new tokens of sequence b go to its
+// last n_new positions, the slot of each read from the block table.
+//
 // One thread moves 8 consecutive elements of one (token, KV head) row, so a
 // row of D elements takes D/8 threads and the K and V pools are written by
 // the same launch (blockIdx.y selects K or V).
@@ -82,11 +85,32 @@ paged_append_kernel(AppendArgs a)
     const int64_t c = gid % chunks_per_row;
     const int64_t h = (gid / chunks_per_row) % a.kv_heads;
     const int64_t t = gid / (chunks_per_row * a.kv_heads);
-    const int64_t slot = a.slot_mapping[t];
+    const bool lead = c == 0 && h == 0 && !is_v;
+    int64_t slot;
+    if (a.slot_mapping) {
+        slot = a.slot_mapping[t];
+    } else {
+        // tail mode: the slot of position L_b - n_new + i from the block table
+        const int64_t b = t / a.n_new, i = t - b * a.n_new;
+        const int64_t L = a.seq_lens[b];
+        const int64_t pos = L - a.n_new + i;
+        if (pos < 0 || L > (int64_t)a.max_pages * a.page_tokens) {
+            if (lead)
+                flag_error(a.dev_err, NBX_DEVERR_SEQ_RANGE);
+            return;
+        }
+        const int32_t page = a.block_table[b * a.max_pages + pos / a.page_tokens];
+        if (page < 0 || page >= a.num_pages) {
+            if (lead)
+                flag_error(a.dev_err, NBX_DEVERR_PAGE_RANGE);
+            return;
+        }
+        slot = (int64_t)page * a.page_tokens + pos % a.page_tokens;
+    }
     if (slot < 0)
         return;                                            // padding token
     if (slot >= (int64_t)a.num_pages * a.page_tokens) {
-        if (c == 0 && h == 0 && !is_v)
+        if (lead)
             flag_error(a.dev_err, NBX_DEVERR_SLOT_RANGE);
         return;
     }

@@ -19,8 +19,12 @@ struct AppendArgs {
     void *v_data;
     int64_t v_stride_page, v_stride_head, v_stride_token;
     float k_scale, v_scale;
-    const int32_t *slot_mapping;
+    const int32_t *slot_mapping;    // null: tail mode (below)
     int32_t *dev_err;
+    // tail mode: token t = b * n_new + i goes to position seq_lens[b] - n_new + i
+    // of sequence b, its slot read from the block table
+    const int32_t *seq_lens, *block_table;
+    int32_t max_pages, n_new;
 };
 
 struct PartialArgs {
@@ -42,6 +46,11 @@ struct PartialArgs {
     int32_t split_size, n_split;
     float *o_part, *m_part, *l_part;
     int32_t *dev_err;
+    // single-launch step (persistent decode kernel): the n_new new positions
+    // of each sequence, [batch, n_new, kv_heads, head_dim] of new_dtype, are
+    // written by the wave that owns the item holding them
+    const void *new_k, *new_v;
+    int32_t new_dtype, n_new;
 };
 
 struct MergeArgs {
@@ -55,6 +64,9 @@ struct MergeArgs {
 hipError_t launch_append(const AppendArgs &a, hipStream_t stream);
 hipError_t launch_partial_valu(const PartialArgs &a, hipStream_t stream);
 hipError_t launch_partial_mfma(const PartialArgs &a, hipStream_t stream);
+// true when launch_partial_mfma runs `a` as one persistent launch, so that it
+// can also perform the append of a.new_k / a.new_v
+bool partial_mfma_is_persistent(const PartialArgs &a);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t stream);
 
 }  // namespace nbx

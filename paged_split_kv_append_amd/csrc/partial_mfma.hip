@@ -415,6 +415,33 @@ decode_mfma_kernel(PartialArgs a)
 
 // ------------------------------------------------------------------ persistent decode
 
+// One new K or V row (D elements at src of a [.., D] array of src_dtype)
+// stored at element offset dst of a bf16 or fp8 pool, with the append's
+// conversions: bf16 -> bf16 bit copy, fp32 -> bf16 round to nearest even, to
+// fp8 the correctly rounded quotient value / scale, rounded to nearest even
+// and saturated.  Lane l stores elements l * D/64 .. (l + 1) * D/64 - 1.
+template <int D, int KVT>
+__device__ __forceinline__ void store_new_row(const void *src_base, int src_dtype, int64_t src,
+                                              void *pool, int64_t dst, float scale, int lane)
+{
+    constexpr int E = D / 64;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int64_t i = lane * E + e;
+        if constexpr (KVT == NBX_BF16) {
+            const uint16_t bits = src_dtype == NBX_BF16
+                                      ? ((const uint16_t *)src_base)[src + i]
+                                      : f32_to_bf16_bits(((const float *)src_base)[src + i]);
+            ((uint16_t *)pool)[dst + i] = bits;
+        } else {
+            const float x = src_dtype == NBX_BF16
+                                ? bf16_bits_to_f32(((const uint16_t *)src_base)[src + i])
+                                : ((const float *)src_base)[src + i];
+            ((uint8_t *)pool)[dst + i] = f32_to_e4m3(__fdiv_rn(x, scale));
+        }
+    }
+}
+
 constexpr int kPersistMaxBatch = 256;      // sequences covered by the lane-register item table
 
 // One wave per work item = (sequence b, split s, KV head g) with keys in the
@@ -427,7 +454,7 @@ constexpr int kPersistMaxBatch = 256;      // sequences covered by the lane-regi
 // and page ids) in flight while the current chunk is computed, so the cost of
 // starting a wave is paid once, not once per split.  Splits without keys get
 // m = -inf and l = 0; their o is not written.
-template <int D, int KVT, bool PVS, int NB>
+template <int D, int KVT, bool PVS, int NB, bool FA>
 __global__ void __launch_bounds__(64)
 decode_persistent_kernel(PartialArgs a)
 {
@@ -458,7 +485,7 @@ decode_persistent_kernel(PartialArgs a)
                     flag_error(a.dev_err, NBX_DEVERR_SEQ_RANGE);
                 L = L < 0 ? 0 : cap;
             }
-            if (wv == 0 && L > NS * S)
+            if (wv == 0 && (L > NS * S || (FA && L < a.n_new)))
                 flag_error(a.dev_err, NBX_DEVERR_SEQ_RANGE);
         }
         int nmax = a.causal ? L - a.q_rows + min(M, a.q_rows) : L;
@@ -506,7 +533,7 @@ decode_persistent_kernel(PartialArgs a)
         return;
 
     struct Item {
-        int b, gk, s, j0, jend, e_j, nchunk;
+        int b, gk, s, j0, jend, e_j, nchunk, L;
         int64_t row_base;
     };
     auto make_item = [&](int k) {
@@ -533,7 +560,35 @@ decode_persistent_kernel(PartialArgs a)
         }
         it.e_j = min(it.jend, n_j);
         it.row_base = ((int64_t)it.b * a.q_heads + (int64_t)it.gk * a.group) * a.q_rows;
+        it.L = L;
         return it;
+    };
+    // Fused append: the new positions L - n_new .. L - 1 that fall in the item
+    // are written to the pools (the conversions of the append kernel) before
+    // any load of the item is issued.  Only this wave reads the item's tiles,
+    // and a wave's memory operations are performed in order, so its later
+    // tile loads see the new rows.
+    auto append_item = [&](const Item &it) {
+        if constexpr (FA) {
+            const int first = it.L - a.n_new;
+            const int lo = max(it.j0, max(first, 0)), hi = min(it.j0 + S, it.L);
+            for (int p = lo; p < hi; ++p) {
+                const int page = tile_page(a, it.b, p, hi, lane == 0);
+                if (page < 0)
+                    continue;
+                const int64_t src = (((int64_t)it.b * a.n_new + (p - first)) * H + it.gk) * D;
+                const int64_t r = p % a.page_tokens;
+                store_new_row<D, KVT>(a.new_k, a.new_dtype, src, (void *)a.k_data,
+                                      (int64_t)page * a.k_stride_page + it.gk * a.k_stride_head +
+                                          r * a.k_stride_token,
+                                      a.k_scale, lane);
+                store_new_row<D, KVT>(a.new_v, a.new_dtype, src, (void *)a.v_data,
+                                      (int64_t)page * a.v_stride_page + it.gk * a.v_stride_head +
+                                          r * a.v_stride_token,
+                                      a.v_scale, lane);
+            }
+            asm volatile("" ::: "memory");     // keep the tile loads after the stores
+        }
     };
     auto load_q = [&](const Item &it, u32x4 (&qv)[KK]) {
 #pragma unroll
@@ -613,6 +668,7 @@ decode_persistent_kernel(PartialArgs a)
 
     int i_item = 0;
     Item cur = make_item(wv);
+    append_item(cur);
     int pg_reg = item_pages(cur, 0), pg_next = -1;
     Item nxt = cur;
     bool has_next = false;
@@ -621,6 +677,7 @@ decode_persistent_kernel(PartialArgs a)
         has_next = i_item + 1 < k_per && kn < N;
         if (has_next) {
             nxt = make_item(kn);
+            append_item(nxt);
             pg_next = item_pages(nxt, 0);
         }
     };
@@ -962,7 +1019,7 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
 
 // Waves the current device holds at once for the persistent decode kernel
 // (resident workgroups per CU x CUs), cached per device.
-template <int D, int KVT, bool PVS, int NB>
+template <int D, int KVT, bool PVS, int NB, bool FA>
 int persistent_waves()
 {
     constexpr int kMaxDev = 64;
@@ -977,7 +1034,7 @@ int persistent_waves()
     }
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void *>(&decode_persistent_kernel<D, KVT, PVS, NB>), 64,
+            &per_cu, reinterpret_cast<const void *>(&decode_persistent_kernel<D, KVT, PVS, NB, FA>), 64,
             0) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
@@ -987,25 +1044,38 @@ int persistent_waves()
     return v;
 }
 
+template <int D, int KVT, bool PVS, int NB, bool FA>
+hipError_t launch_persistent(const PartialArgs &a, hipStream_t stream)
+{
+    const int64_t items = (int64_t)a.batch * a.kv_heads * a.n_split;
+    const int waves = persistent_waves<D, KVT, PVS, NB, FA>();
+    if (waves <= 0)
+        return hipErrorInvalidConfiguration;
+    const int grid = (int)(items < waves ? items : waves);
+    hipLaunchKernelGGL((decode_persistent_kernel<D, KVT, PVS, NB, FA>), dim3(grid), dim3(64), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+bool persistent_shape(const PartialArgs &a)
+{
+    return a.rows_per_kv <= 16 && a.batch <= kPersistMaxBatch;
+}
+
 template <int D, int KVT, bool PVS>
 hipError_t launch_kind(const PartialArgs &a, hipStream_t stream)
 {
     const int M = a.rows_per_kv;
-    if (M <= 16 && a.batch <= kPersistMaxBatch) {
-        const int64_t items = (int64_t)a.batch * a.kv_heads * a.n_split;
-        const int waves = a.batch <= 64 ? persistent_waves<D, KVT, PVS, 1>()
-                                        : persistent_waves<D, KVT, PVS, 4>();
-        if (waves <= 0)
-            return hipErrorInvalidConfiguration;
-        const int grid = (int)(items < waves ? items : waves);
+    if (persistent_shape(a)) {
+        const bool fa = a.new_k != nullptr && a.n_new > 0;
         if (a.batch <= 64)
-            hipLaunchKernelGGL((decode_persistent_kernel<D, KVT, PVS, 1>), dim3(grid), dim3(64),
-                               0, stream, a);
-        else
-            hipLaunchKernelGGL((decode_persistent_kernel<D, KVT, PVS, 4>), dim3(grid), dim3(64),
-                               0, stream, a);
-        return hipGetLastError();
+            return fa ? launch_persistent<D, KVT, PVS, 1, true>(a, stream)
+                      : launch_persistent<D, KVT, PVS, 1, false>(a, stream);
+        return fa ? launch_persistent<D, KVT, PVS, 4, true>(a, stream)
+                  : launch_persistent<D, KVT, PVS, 4, false>(a, stream);
     }
+    if (a.new_k != nullptr && a.n_new > 0)
+        return hipErrorInvalidValue;           // the caller appends first for these shapes
     if (M <= 16) {
         // waves per (split, head): enough that each wave's run of chunks is short
         const int chunks = (a.split_size + kChunk - 1) / kChunk;
@@ -1053,6 +1123,8 @@ hipError_t launch_d(const PartialArgs &a, hipStream_t stream)
 }
 
 }  // namespace
+
+bool partial_mfma_is_persistent(const PartialArgs &a) { return persistent_shape(a); }
 
 hipError_t launch_partial_mfma(const PartialArgs &a, hipStream_t stream)
 {

@@ -53,6 +53,25 @@ class DevCase:
                             n_split, ws, out, causal=c.causal, dev_err=self.err)
         return out.reshape(rows, c.head_dim)
 
+    def step(self, new_k=None, new_v=None, n_split=None, split_size=None,
+             out_dtype=torch.float32):
+        """nbx_paged_decode_step; new_k / new_v [batch, n_new, kv_heads, D] (default: the
+        case's own new tokens, one per sequence)."""
+        if n_split is None:
+            n_split, split_size = self.plan()
+        c = self.case
+        if new_k is None and self.new_k is not None:
+            new_k, new_v = self.new_k.unsqueeze(1), self.new_v.unsqueeze(1)
+        kp, vp = self.pools()
+        dev = self.q.device
+        ws = torch.empty(nb.nbx_paged_decode_workspace_bytes(c.rows, n_split, c.head_dim),
+                         dtype=torch.uint8, device=dev)
+        out = torch.empty(c.batch, c.q_heads, c.q_rows, c.head_dim, dtype=out_dtype, device=dev)
+        nb.nbx_paged_decode_step(self.q, kp, vp, self.bt, self.lens, c.softmax_scale, split_size,
+                                 n_split, ws, out, new_k=new_k, new_v=new_v, causal=c.causal,
+                                 dev_err=self.err)
+        return out.reshape(c.rows, c.head_dim)
+
     def partial(self, n_split=None, split_size=None):
         if n_split is None:
             n_split, split_size = self.plan()

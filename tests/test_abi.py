@@ -134,3 +134,23 @@ def test_one_call_workspace_checks(lib):
     assert call(None, need) == -5
     assert call(FAKE, need - 1) == -5
     assert call(FAKE + 16, need) == -5
+
+
+def test_step_validation(lib):
+    k, v = pool(), pool()
+    need = nb.nbx_paged_decode_workspace_bytes(8, 2, 128)
+
+    def call(nk=FAKE, nv=FAKE, ndt=1, n_new=1, ws=FAKE, nbytes=need, out=FAKE, odt=0):
+        return lib.nbx_paged_decode_step(
+            FAKE, 1, 2, 4, 1, 0, nk, nv, ndt, n_new, ctypes.byref(k), ctypes.byref(v), FAKE, 4,
+            FAKE, 0.1, 256, 2, ws, nbytes, out, odt, None, None)
+    assert call(nk=None) == -1
+    assert call(nv=None) == -1
+    assert call(ndt=2) == -2
+    assert call(odt=2) == -2
+    assert call(n_new=-1) == -3
+    assert call(nk=FAKE + 8) == -4
+    assert call(out=FAKE + 4) == -4
+    assert call(ws=None) == -5
+    assert call(nbytes=need - 1) == -5
+    assert call(ws=FAKE + 16) == -5

@@ -1,0 +1,217 @@
+"""GPU parity of nbx_paged_decode_step (append at each sequence's last
+positions, then partial and merge, in one launch where the shape allows)
+against the float64 oracle's append followed by its attention.
+
+The slots the step fills hold NaN beforehand, so an output computed from the
+old contents of a slot is not finite; the pools after the step are compared
+bit for bit with the oracle's append."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_split_kv_append_amd import binding as nb
+from paged_split_kv_append_amd import synth
+
+from gpu_cases import TOL, DevCase, max_abs
+
+pytestmark = pytest.mark.gpu
+
+REDUCED = {
+    2: dict(batch=6, lens=("uniform", 1, 700)),
+    5: dict(batch=3, lens=("loguniform", 100, 3000)),
+}
+
+
+def _pool_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.uint8).numpy().reshape(-1)
+
+
+def _bytes(a: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(a).view(np.uint8).reshape(-1)
+
+
+def _tail_slots(case, n_new):
+    """Slots of positions L_b - n_new .. L_b - 1 of every sequence, [batch * n_new]."""
+    T = case.page_tokens
+    out = []
+    for b in range(case.batch):
+        for i in range(n_new):
+            pos = int(case.seq_lens[b]) - n_new + i
+            out.append(int(case.block_table[b, pos // T]) * T + pos % T)
+    return np.array(out, dtype=np.int32)
+
+
+def _poison_slots(case, slots):
+    for pool, dt in ((case.k_pool, case.kv_dtype), (case.v_pool, case.kv_dtype)):
+        nan = synth.nan_bits(dt, pool)
+        for s in slots:
+            pool[s // case.page_tokens, :, s % case.page_tokens, :] = nan
+
+
+def _check_step(case, dc, out, new_k, new_v, slots):
+    """Output against the oracle after its append of new_k/new_v at `slots`; pools bitwise."""
+    n_tok = new_k.shape[0] * new_k.shape[1]
+    H, D = case.kv_heads, case.head_dim
+    nk = new_k.float().cpu().reshape(n_tok, H, D)
+    nv = new_v.float().cpu().reshape(n_tok, H, D)
+    kp, bk = oracle.append(nk, "f32", case.k_pool, case.kv_dtype, case.k_scale, case.page_tokens,
+                           slots)
+    vp, bv = oracle.append(nv, "f32", case.v_pool, case.kv_dtype, case.v_scale, case.page_tokens,
+                           slots)
+    assert bk == 0 and bv == 0
+    assert np.array_equal(_pool_bits(dc.k), _bytes(kp))
+    assert np.array_equal(_pool_bits(dc.v), _bytes(vp))
+    ref = oracle.attention(case.q, case.q_dtype, kp, vp, case.kv_dtype, case.block_table,
+                           case.seq_lens, case.softmax_scale, case.causal, case.k_scale,
+                           case.v_scale)
+    assert torch.isfinite(out).all()
+    err = max_abs(out, ref)
+    assert err <= TOL[case.kv_dtype], f"max abs err {err}"
+
+
+@pytest.mark.parametrize("workload", [2, 5])
+@pytest.mark.parametrize("seed", [None, 103])
+def test_step_single_launch_matches_oracle(workload, seed):
+    case = synth.make_case(workload, seed=seed, **REDUCED[workload])
+    print(f"step workload={workload} seed={seed} lens={case.seq_lens.tolist()}", flush=True)
+    dc = DevCase(case)
+    out = dc.step()
+    torch.cuda.synchronize()
+    assert dc.err_bits() == 0
+    _check_step(case, dc, out, case.new_k.unsqueeze(1), case.new_v.unsqueeze(1),
+                case.slot_mapping)
+
+
+@pytest.mark.parametrize("new_dtype", [torch.float32, torch.bfloat16])
+def test_step_bf16_new_tokens_and_fp8_pool(new_dtype):
+    """bf16 new tokens (bit copy into a bf16 pool) and fp32/bf16 tokens into an fp8 pool."""
+    for pool_dtype in ("bf16", "fp8"):
+        case = synth.make_case(2, seed=41, kv_dtype=pool_dtype, batch=5, lens=("uniform", 1, 500))
+        print(f"step new={new_dtype} pool={pool_dtype}", flush=True)
+        dc = DevCase(case)
+        nk = case.new_k.to(new_dtype).unsqueeze(1).cuda()
+        nv = case.new_v.to(new_dtype).unsqueeze(1).cuda()
+        out = dc.step(nk, nv)
+        torch.cuda.synchronize()
+        assert dc.err_bits() == 0
+        _check_step(case, dc, out, nk, nv, case.slot_mapping)
+
+
+def test_step_window_append_multirow_path():
+    """16 new positions per sequence with 16 causal rows (a verify window): the
+    shape runs the append, multi-row partial and merge kernels in turn."""
+    case = synth.make_case(3, seed=44, batch=2, lens=("uniform", 300, 900))
+    n_new = case.q_rows
+    slots = _tail_slots(case, n_new)
+    _poison_slots(case, slots)
+    g = torch.Generator().manual_seed(44)
+    shape = (case.batch, n_new, case.kv_heads, case.head_dim)
+    nk = torch.randn(shape, generator=g)
+    nv = torch.randn(shape, generator=g)
+    dc = DevCase(case)
+    out = dc.step(nk.cuda(), nv.cuda())
+    torch.cuda.synchronize()
+    assert dc.err_bits() == 0
+    _check_step(case, dc, out, nk, nv, slots)
+
+
+def test_step_fp32_pool_vector_path():
+    case = synth.make_case(1, append=True)
+    dc = DevCase(case)
+    out = dc.step()
+    torch.cuda.synchronize()
+    assert dc.err_bits() == 0
+    _check_step(case, dc, out, case.new_k.unsqueeze(1), case.new_v.unsqueeze(1),
+                case.slot_mapping)
+
+
+def test_step_two_new_positions_across_a_split_boundary():
+    """n_new = 2 with the two positions in different splits (and items)."""
+    case = synth.make_case(2, seed=45, append=False, batch=4, lens=("fixed", 257))
+    n_new = 2                                  # positions 255 and 256: splits 0 and 1 at S=256
+    slots = _tail_slots(case, n_new)
+    _poison_slots(case, slots)
+    g = torch.Generator().manual_seed(45)
+    shape = (case.batch, n_new, case.kv_heads, case.head_dim)
+    nk = torch.randn(shape, generator=g)
+    nv = torch.randn(shape, generator=g)
+    dc = DevCase(case)
+    out = dc.step(nk.cuda(), nv.cuda(), n_split=2, split_size=256)
+    torch.cuda.synchronize()
+    assert dc.err_bits() == 0
+    _check_step(case, dc, out, nk, nv, slots)
+
+
+def test_step_without_new_tokens_equals_decode_bitwise():
+    case = synth.make_case(2, seed=46, append=False, batch=6, lens=("uniform", 1, 700))
+    a = DevCase(case).decode()
+    b = DevCase(case).step()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_step_is_bitwise_repeatable_and_equals_two_call_path():
+    case = synth.make_case(2, seed=47, batch=6, lens=("uniform", 1, 700))
+    d1, d2 = DevCase(case), DevCase(case)
+    s1 = d1.step()
+    s2 = d2.step()
+    d3 = DevCase(case)
+    d3.append()
+    ref = d3.decode()
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)
+    assert torch.equal(s1, ref)
+    # pools hold NaN poison in unused slots: compare their bytes
+    assert np.array_equal(_pool_bits(d1.k), _pool_bits(d3.k))
+    assert np.array_equal(_pool_bits(d1.v), _pool_bits(d3.v))
+
+
+def test_step_sequence_shorter_than_new_tokens_is_flagged():
+    case = synth.make_case(2, seed=48, batch=3, lens=("fixed", 40))
+    case.seq_lens[1] = 0
+    dc = DevCase(case)
+    out = dc.step()
+    torch.cuda.synchronize()
+    assert dc.err_bits() & 0x4
+    H = case.q_heads
+    assert torch.all(out[H:2 * H] == 0)
+    keep = [0, 2]
+    kp, _ = oracle.append(case.new_k[keep], "f32", case.k_pool, case.kv_dtype, 1.0,
+                          case.page_tokens, case.slot_mapping[keep])
+    vp, _ = oracle.append(case.new_v[keep], "f32", case.v_pool, case.kv_dtype, 1.0,
+                          case.page_tokens, case.slot_mapping[keep])
+    ref = oracle.attention(case.q, case.q_dtype, kp, vp, case.kv_dtype, case.block_table,
+                           case.seq_lens, case.softmax_scale)
+    assert max_abs(out, ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("workload", [2, 5])
+def test_step_full_size_against_oracle(workload):
+    case = synth.make_case(workload)
+    print(f"full-size step workload={workload} kv_bytes={case.kv_bytes()}", flush=True)
+    dc = DevCase(case)
+    out = dc.step()
+    torch.cuda.synchronize()
+    assert dc.err_bits() == 0
+    _check_step(case, dc, out, case.new_k.unsqueeze(1), case.new_v.unsqueeze(1),
+                case.slot_mapping)
+
+
+def test_step_partials_only_then_merge_equals_full_step():
+    case = synth.make_case(2, seed=49, batch=6, lens=("uniform", 1, 700))
+    n_split, split = DevCase(case).plan()
+    full = DevCase(case).step()
+    dc = DevCase(case)
+    kp, vp = dc.pools()
+    ws = torch.empty(nb.nbx_paged_decode_workspace_bytes(case.rows, n_split, case.head_dim),
+                     dtype=torch.uint8, device="cuda")
+    nb.nbx_paged_decode_step(dc.q, kp, vp, dc.bt, dc.lens, case.softmax_scale, split, n_split,
+                             ws, None, new_k=dc.new_k.unsqueeze(1), new_v=dc.new_v.unsqueeze(1),
+                             dev_err=dc.err)
+    o, m, l = nb.workspace_partials(ws, case.rows, n_split, case.head_dim)
+    out = torch.empty(case.rows, case.head_dim, device="cuda")
+    nb.nbx_paged_decode_merge(o, m, l, out)
+    torch.cuda.synchronize()
+    assert dc.err_bits() == 0
+    assert torch.equal(out, full)
