@@ -215,3 +215,16 @@ def test_step_partials_only_then_merge_equals_full_step():
     torch.cuda.synchronize()
     assert dc.err_bits() == 0
     assert torch.equal(out, full)
+
+
+def test_step_bf16_output():
+    case = synth.make_case(2, seed=53, batch=4, lens=("uniform", 1, 600))
+    dc = DevCase(case)
+    out = dc.step(out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    kp, vp, _ = oracle.case_append(case)
+    ref = oracle.attention(case.q, case.q_dtype, kp, vp, case.kv_dtype, case.block_table,
+                           case.seq_lens, case.softmax_scale)
+    err = np.abs(out.double().cpu().numpy().reshape(ref.shape) - ref)
+    half_ulp = np.abs(ref) * 2.0 ** -8
+    assert np.all(err <= TOL["bf16"] + half_ulp)
