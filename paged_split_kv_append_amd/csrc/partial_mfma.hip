@@ -568,12 +568,15 @@ decode_persistent_kernel(PartialArgs a)
     // any load of the item is issued.  Only this wave reads the item's tiles,
     // and a wave's memory operations are performed in order, so its later
     // tile loads see the new rows.
-    auto append_item = [&](const Item &it) {
+    // `pg` holds the page ids of the item's first 32 chunks (item_pages(it, 0)).
+    auto append_item = [&](const Item &it, int pg) {
         if constexpr (FA) {
             const int first = it.L - a.n_new;
             const int lo = max(it.j0, max(first, 0)), hi = min(it.j0 + S, it.L);
             for (int p = lo; p < hi; ++p) {
-                const int page = tile_page(a, it.b, p, hi, lane == 0);
+                const int tl = (p - it.j0) >> 4;           // tile of p within the item
+                const int page = tl < 64 ? __builtin_amdgcn_readlane(pg, tl)
+                                         : tile_page(a, it.b, p, hi, lane == 0);
                 if (page < 0)
                     continue;
                 const int64_t src = (((int64_t)it.b * a.n_new + (p - first)) * H + it.gk) * D;
@@ -668,8 +671,8 @@ decode_persistent_kernel(PartialArgs a)
 
     int i_item = 0;
     Item cur = make_item(wv);
-    append_item(cur);
     int pg_reg = item_pages(cur, 0), pg_next = -1;
+    append_item(cur, pg_reg);
     Item nxt = cur;
     bool has_next = false;
     auto prepare_next = [&]() {
@@ -677,8 +680,8 @@ decode_persistent_kernel(PartialArgs a)
         has_next = i_item + 1 < k_per && kn < N;
         if (has_next) {
             nxt = make_item(kn);
-            append_item(nxt);
             pg_next = item_pages(nxt, 0);
+            append_item(nxt, pg_next);
         }
     };
     int c = 0;
