@@ -49,67 +49,56 @@ __device__ __forceinline__ i32x4 make_buffer_rsrc(const void *base, uint32_t byt
     return r;
 }
 
-// 8 consecutive pool elements at byte offset `voff` of a buffer, as 8 bf16
-template <int KVT>
-__device__ __forceinline__ u32x4 buffer_load8_bf16(i32x4 rsrc, int voff);
-
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// E4M3FN code (low byte of c) -> bf16 bits, exact.  The 7 magnitude bits are
-// placed as the exponent/mantissa of an fp32 with bias 127 instead of 7 and the
-// value rescaled by 2^120 (subnormal codes become fp32 denormals, which the
-// multiply keeps); at most 4 significant bits, so the top half is the bf16.
-__device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t c)
+// 8 E4M3FN codes (two dwords) widened to 8 bf16 (four dwords), exactly: every
+// E4M3FN value (subnormals included) is a bf16 value, so the hardware
+// conversion with scale 1 is exact; NaN codes give NaN.  Byte 2 k + h of a
+// dword lands in half h of result dword 2 k (bytes 0, 1) or 2 k + 1 (bytes 2, 3).
+__device__ __forceinline__ u32x4 widen8_e4m3(u32x2 w)
 {
-    const uint32_t em = c & 0x7Fu;
-    const float f = __uint_as_float(em << 20) * 0x1p120f;
-    uint32_t b = __float_as_uint(f) >> 16;
-    b = em == 0x7Fu ? 0x7FC0u : b;
-    return b | ((c & 0x80u) << 8);
-}
-
-// 8 consecutive elements of a pool row at element index i, as 8 bf16 (4 dwords)
-template <int KVT>
-__device__ __forceinline__ u32x4 load8_bf16(const void *base, int64_t i)
-{
-    if constexpr (KVT == NBX_BF16) {
-        return *(const u32x4 *)((const uint16_t *)base + i);
-    } else {
-        const u32x2 w = *(const u32x2 *)((const uint8_t *)base + i);
-        u32x4 r;
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const uint32_t x = w[k];
-            r[2 * k] = e4m3_to_bf16_bits(x & 0xFFu) | (e4m3_to_bf16_bits((x >> 8) & 0xFFu) << 16);
-            r[2 * k + 1] =
-                e4m3_to_bf16_bits((x >> 16) & 0xFFu) | (e4m3_to_bf16_bits(x >> 24) << 16);
-        }
-        return r;
-    }
-}
-
-template <>
-__device__ __forceinline__ u32x4 buffer_load8_bf16<NBX_BF16>(i32x4 rsrc, int voff)
-{
-    return nbx_buffer_load_b128(rsrc, voff, 0, 0);
-}
-
-template <>
-__device__ __forceinline__ u32x4 buffer_load8_bf16<NBX_FP8_E4M3>(i32x4 rsrc, int voff)
-{
-    const u32x2 w = nbx_buffer_load_b64(rsrc, voff, 0, 0);
     u32x4 r;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-        const uint32_t x = w[k];
-        r[2 * k] = e4m3_to_bf16_bits(x & 0xFFu) | (e4m3_to_bf16_bits((x >> 8) & 0xFFu) << 16);
-        r[2 * k + 1] = e4m3_to_bf16_bits((x >> 16) & 0xFFu) | (e4m3_to_bf16_bits(x >> 24) << 16);
+        r[2 * k] =
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[k], 1.0f, false));
+        r[2 * k + 1] =
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[k], 1.0f, true));
     }
     return r;
+}
+
+// 8 consecutive pool elements as loaded (8 bf16 or 8 E4M3FN codes) and their
+// bf16 form
+template <int KVT>
+struct KvRaw {
+    using type = u32x4;
+};
+template <>
+struct KvRaw<NBX_FP8_E4M3> {
+    using type = u32x2;
+};
+
+template <int KVT>
+__device__ __forceinline__ typename KvRaw<KVT>::type buffer_load8_raw(i32x4 rsrc, int voff)
+{
+    if constexpr (KVT == NBX_BF16)
+        return nbx_buffer_load_b128(rsrc, voff, 0, 0);
+    else
+        return nbx_buffer_load_b64(rsrc, voff, 0, 0);
+}
+
+template <int KVT>
+__device__ __forceinline__ u32x4 as_bf16x8(typename KvRaw<KVT>::type r)
+{
+    if constexpr (KVT == NBX_BF16)
+        return r;
+    else
+        return widen8_e4m3(r);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)

@@ -130,19 +130,6 @@ __device__ __forceinline__ u32x4 vt_operand(const uint8_t *lane_base, int dt)
     return u32x4{ua[0], ua[1], ub[0], ub[1]};
 }
 
-// 8 E4M3FN codes (two dwords) widened to 8 bf16 (four dwords), exactly
-__device__ __forceinline__ u32x4 widen8_e4m3(u32x2 w)
-{
-    u32x4 r;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const uint32_t x = w[k];
-        r[2 * k] = e4m3_to_bf16_bits(x & 0xFFu) | (e4m3_to_bf16_bits((x >> 8) & 0xFFu) << 16);
-        r[2 * k + 1] = e4m3_to_bf16_bits((x >> 16) & 0xFFu) | (e4m3_to_bf16_bits(x >> 24) << 16);
-    }
-    return r;
-}
-
 // Online-softmax step for one lane's row over the 32 positions of a chunk:
 // sc holds the scaled scores (log2 units, -inf where masked).  Updates m, l,
 // rescales o and returns the P operand (hi and residual lo parts).
@@ -170,9 +157,11 @@ __device__ __forceinline__ void softmax_step(float (&sc)[2][4], float &m_run, fl
         }
     l_run = l_run * corr + psum;
     m_run = m_new;
+    if (__any(corr != 1.0f)) {             // a row's max moved: rescale (else o * 1 = o)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-        o[dt] *= corr;
+        for (int dt = 0; dt < DT; ++dt)
+            o[dt] *= corr;
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         ph[2 * t] = pack_bf16(p[t][0], p[t][1]);
@@ -260,7 +249,7 @@ decode_mfma_kernel(PartialArgs a)
     // One register set each for K and V: a chunk's loads are in flight while
     // the previous chunk is computed.  The compiler places the waits.
     int pg_reg = -1;
-    u32x4 kr[2][KK];
+    typename KvRaw<KVT>::type kr[2][KK];       // K as loaded; widened at its use
     u32x4 vr[BF ? DT : 1];
     u32x2 vraw[BF ? 1 : DT];                   // fp8: V codes awaiting widening
     auto pages_of = [&](int q, int &pg0, int &pg1) {
@@ -293,7 +282,7 @@ decode_mfma_kernel(PartialArgs a)
                                             a.page_tokens, t ? pg1 : pg0, p0 + 16 * t, 16);
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk)
-                kr[t][kk] = buffer_load8_bf16<KVT>(rk, k_lane + kk * 32 * ESZ);
+                kr[t][kk] = buffer_load8_raw<KVT>(rk, k_lane + kk * 32 * ESZ);
         }
     };
     auto land_v = [&]() {
@@ -334,7 +323,7 @@ decode_mfma_kernel(PartialArgs a)
                 f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk)
-                    acc = mfma_bf16(kr[t][kk], qb[kk], acc);
+                    acc = mfma_bf16(as_bf16x8<KVT>(kr[t][kk]), qb[kk], acc);
                 const bool tv = (t ? cur1 : cur0) >= 0;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -614,7 +603,8 @@ decode_persistent_kernel(PartialArgs a)
     const float scale2 = a.scale * a.k_scale * kLog2e;
     const float vs = a.v_scale;
 
-    u32x4 kr[2][KK], qb[KK];
+    typename KvRaw<KVT>::type kr[2][KK];       // K as loaded; widened at its use
+    u32x4 qb[KK];
     u32x4 vr[BF ? DT : 1];
     u32x2 vraw[BF ? 1 : DT];
     auto issue_v = [&](const Item &it, int c, int pg0, int pg1) {
@@ -647,7 +637,7 @@ decode_persistent_kernel(PartialArgs a)
                                             a.page_tokens, t ? pg1 : pg0, p0 + 16 * t, 16);
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk)
-                kr[t][kk] = buffer_load8_bf16<KVT>(rk, k_lane + kk * 32 * ESZ);
+                kr[t][kk] = buffer_load8_raw<KVT>(rk, k_lane + kk * 32 * ESZ);
         }
     };
     auto land_v = [&]() {
@@ -722,7 +712,7 @@ decode_persistent_kernel(PartialArgs a)
             f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk)
-                acc = mfma_bf16(kr[t][kk], qb[kk], acc);
+                acc = mfma_bf16(as_bf16x8<KVT>(kr[t][kk]), qb[kk], acc);
             const bool tv = (t ? cpg1 : cpg0) >= 0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -770,18 +760,29 @@ decode_persistent_kernel(PartialArgs a)
 
 // ------------------------------------------------------------------ multi-row
 
-template <int D, int KVT, bool PVS, int RW, int NT>
-__global__ void __launch_bounds__(RW * 64)
+// A workgroup of 8 waves takes 8 x NT row tiles of 16 rows of one (sequence,
+// KV head, split).  The 2 K tiles and 2 V tiles of a 32-position chunk are
+// 2 KK + DT pieces of 1 KB (as bf16); wave w loads pieces w, w + 8, ..., so
+// for D = 256 each of its loads has a fixed role (K or V, tile) and one
+// descriptor per tile serves the whole workgroup.  Chunk c + 1 waits in LDS
+// and chunks c + 2, c + 3 in registers while chunk c is computed; one barrier
+// per chunk.  K is stored in LDS with a 16-byte swizzle inside each 1 KB
+// block (row r, piece p at unit 4 r + ((p + r / 4) & 3)), so that the 16
+// lanes of a group reading one 16-byte operand piece each cover all banks.
+template <int D, int KVT, bool PVS, int NT>
+__global__ void __launch_bounds__(512)
 multirow_mfma_kernel(PartialArgs a, int row_blocks)
 {
+    constexpr int RW = 8;                      // waves per workgroup
     constexpr int KK = D / 32, DT = D / 16;
     constexpr bool BF = KVT == NBX_BF16;
     constexpr int ESZ = BF ? 2 : 1;
     constexpr int KBYTES = kChunk * 2 * D;     // K chunk as bf16: [tile][KK][16 rows][64 B]
     constexpr int VBYTES = kChunk * 2 * D;     // V chunk as bf16: [tile][DT][16 rows][32 B]
     constexpr int BUF = KBYTES + VBYTES;
-    constexpr int NI = 2 * KK + DT;            // 1 KB (bf16) loads per chunk: K then V
-    constexpr int MYI = (NI + RW - 1) / RW;    // upper bound of one wave's share
+    constexpr int NI = 2 * KK + DT;            // 1 KB (bf16) pieces per chunk: K then V
+    constexpr int PER = NI / RW;               // pieces per wave
+    static_assert(NI % RW == 0, "pieces per chunk must split evenly over the waves");
     constexpr int R = RW * NT * 16;            // rows per workgroup
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF];
 
@@ -798,6 +799,8 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
     const int row_lo = rb * R, row_hi = min(M, row_lo + R);
     const int64_t row_base = ((int64_t)b * a.q_heads + (int64_t)gk * a.group) * a.q_rows;
     const bool lead = threadIdx.x == 0;
+    // a wave whose row tiles are all past the last row loads its share only
+    const bool has_rows = row_lo + w * NT * 16 < row_hi;
 
     const int L = clamp_len(a, b, lead && s == 0 && rb == 0);
     if (lead && rb == 0 && s == a.n_split - 1 && L > a.n_split * a.split_size)
@@ -849,10 +852,13 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
     const int64_t k_head = (int64_t)gk * a.k_stride_head;
     const int64_t v_head = (int64_t)gk * a.v_stride_head;
     const int kst_b = (int)(a.k_stride_token * ESZ), vst_b = (int)(a.v_stride_token * ESZ);
-    // fixed per-lane byte offsets inside a tile of the 64-lane loads
+    // fixed per-lane byte offsets of the 64-lane piece loads
     const int k_lane = (lane >> 2) * kst_b + (lane & 3) * 8 * ESZ;   // + kk * 32 * ESZ
     const int v_lane = ((lane & 31) >> 1) * vst_b + ((lane >> 5) * 16 + (lane & 1) * 8) * ESZ;
-    const uint8_t *k_rd = smem + j * 64 + g * 16;                    // + (t*KK + kk) * 1024
+    // LDS: swizzled K store of this lane (row lane / 4, piece lane % 4) and
+    // read of operand piece g of row j; transposed V read
+    const int k_st = (4 * (lane >> 2) + (((lane & 3) + (lane >> 4)) & 3)) * 16;
+    const uint8_t *k_rd = smem + (4 * j + ((g + (j >> 2)) & 3)) * 16;   // + (t*KK + kk) * 1024
     const uint8_t *vt_lane = smem + KBYTES + (4 * g + (j >> 2)) * 32 + (j & 3) * 8;
 
     // page ids of the chunks of even / odd 32-chunk batches (lane i: tile i & 1
@@ -870,63 +876,60 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
         else
             pg_even = v;
     };
-    u32x4 raw16[BF ? MYI : 1];                 // this wave's share of a chunk in flight
-    u32x2 raw8[BF ? 1 : MYI];                  // (fp8: codes, widened when they land)
 
-    // this wave's share of the loads of chunk c: instructions w, w + RW, ...
-    auto issue = [&](int c, uint8_t *buf) {
+    struct Regs {
+        u32x4 r16[BF ? PER : 1];
+        u32x2 r8[BF ? 1 : PER];
+    };
+    // this wave's pieces of chunk c into registers
+    auto issue = [&](int c, Regs &rg) {
         const int p0 = j0 + c * kChunk;
         const int page0 = page_of(c, 0), page1 = page_of(c, 1);
+        const i32x4 rk0 = tile_rsrc<ESZ>(a.k_data, a.k_stride_page, k_head, a.k_stride_token,
+                                         a.page_tokens, page0, p0, 16);
+        const i32x4 rk1 = tile_rsrc<ESZ>(a.k_data, a.k_stride_page, k_head, a.k_stride_token,
+                                         a.page_tokens, page1, p0 + 16, 16);
+        const i32x4 rv0 = tile_rsrc<ESZ>(a.v_data, a.v_stride_page, v_head, a.v_stride_token,
+                                         a.page_tokens, page0, p0, min(16, jend - p0));
+        const i32x4 rv1 = tile_rsrc<ESZ>(a.v_data, a.v_stride_page, v_head, a.v_stride_token,
+                                         a.page_tokens, page1, p0 + 16, min(16, jend - p0 - 16));
 #pragma unroll
-        for (int x = 0; x < MYI; ++x) {
-            const int i = w + x * RW;
-            if (i >= NI)
-                break;
-            const bool isk = i < 2 * KK;
-            const int ii = isk ? i : i - 2 * KK;
-            const int t = isk ? ii / KK : ii / (DT / 2);
-            const int ts = p0 + 16 * t;
-            const int page = t ? page1 : page0;
+        for (int x = 0; x < PER; ++x) {
+            const int i = x * RW + w;
             i32x4 rs;
-            int voff;
-            uint8_t *dst;
-            if (isk) {
-                const int kk = ii % KK;
-                rs = tile_rsrc<ESZ>(a.k_data, a.k_stride_page, k_head, a.k_stride_token,
-                                    a.page_tokens, page, ts, 16);
-                voff = k_lane + kk * 32 * ESZ;
-                dst = buf + (t * KK + kk) * 1024;
+            int off;
+            if (i < 2 * KK) {
+                rs = i < KK ? rk0 : rk1;
+                off = k_lane + (i % KK) * 32 * ESZ;
             } else {
-                const int k = ii % (DT / 2);
-                rs = tile_rsrc<ESZ>(a.v_data, a.v_stride_page, v_head, a.v_stride_token,
-                                    a.page_tokens, page, ts, min(16, jend - ts));
-                voff = v_lane + k * 32 * ESZ;
-                dst = buf + KBYTES + t * DT * 512 + k * 1024;
+                const int ii = i - 2 * KK;
+                rs = ii < DT / 2 ? rv0 : rv1;
+                off = v_lane + (ii % (DT / 2)) * 32 * ESZ;
             }
-            (void)dst;
             if constexpr (BF)
-                raw16[x] = nbx_buffer_load_b128(rs, voff, 0, 0);
+                rg.r16[x] = nbx_buffer_load_b128(rs, off, 0, 0);
             else
-                raw8[x] = nbx_buffer_load_b64(rs, voff, 0, 0);
+                rg.r8[x] = nbx_buffer_load_b64(rs, off, 0, 0);
         }
     };
-    // this wave's share of chunk c landed in registers: write it to the chunk's
-    // LDS buffer (rows outside a descriptor range were read as zeros)
-    auto land = [&](uint8_t *buf) {
+    // this wave's pieces of a chunk, landed in registers, into an LDS buffer
+    // (rows outside a descriptor range were read as zeros)
+    auto land = [&](uint8_t *buf, const Regs &rg) {
 #pragma unroll
-        for (int x = 0; x < MYI; ++x) {
-            const int i = w + x * RW;
-            if (i >= NI)
-                break;
-            const bool isk = i < 2 * KK;
-            const int ii = isk ? i : i - 2 * KK;
-            const int t = isk ? ii / KK : ii / (DT / 2);
-            uint8_t *dst = isk ? buf + (t * KK + ii % KK) * 1024
-                               : buf + KBYTES + t * DT * 512 + (ii % (DT / 2)) * 1024;
+        for (int x = 0; x < PER; ++x) {
+            const int i = x * RW + w;
+            uint8_t *dst;
+            if (i < 2 * KK) {
+                dst = buf + i * 1024 + k_st;              // piece i = t * KK + kk
+            } else {
+                const int ii = i - 2 * KK;
+                const int t = ii / (DT / 2), k = ii % (DT / 2);
+                dst = buf + KBYTES + t * DT * 512 + k * 1024 + lane * 16;
+            }
             if constexpr (BF)
-                *(u32x4 *)(dst + lane * 16) = raw16[x];
+                *(u32x4 *)dst = rg.r16[x];
             else
-                *(u32x4 *)(dst + lane * 16) = widen8_e4m3(raw8[x]);
+                *(u32x4 *)dst = widen8_e4m3(rg.r8[x]);
         }
     };
     auto compute = [&](int c, int boff) {
@@ -973,29 +976,36 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
         }
     };
 
-    // Chunk c + 1 is in registers while chunk c is computed from LDS; after
-    // computing, it lands in the other LDS buffer and chunk c + 2 is issued.
-    // One barrier per chunk: it publishes chunk c and retires buffer (c + 1) & 1.
+    // Iteration c: barrier (chunk c is in LDS buffer c & 1, every wave is done
+    // with chunk c - 1), compute chunk c, land chunk c + 1 (registers) into
+    // buffer (c + 1) & 1, issue chunk c + 3 into the registers just freed.
+    Regs ra, rb2;
+    auto step = [&](int c, Regs &land_regs) {
+        __syncthreads();
+        if (has_rows)
+            compute(c, (c & 1) * BUF);
+        if (c + 1 < nchunk) {
+            land(smem + ((c + 1) & 1) * BUF, land_regs);
+            if (c + 3 < nchunk) {
+                if (((c + 3) & 31) == 0)
+                    refresh(c + 3);
+                issue(c + 3, land_regs);
+            }
+        }
+    };
     if (nchunk > 0) {
         refresh(0);
-        issue(0, smem);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        land(smem);
+        issue(0, ra);
         if (nchunk > 1)
-            issue(1, smem + BUF);
-        for (int c = 0; c < nchunk; ++c) {
-            const int boff = (c & 1) * BUF;
-            __syncthreads();
-            compute(c, boff);
-            if (c + 1 < nchunk) {
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                land(smem + ((c + 1) & 1) * BUF);
-                if (c + 2 < nchunk) {
-                    if (((c + 2) & 31) == 0)
-                        refresh(c + 2);
-                    issue(c + 2, smem + boff);
-                }
-            }
+            issue(1, rb2);
+        land(smem, ra);
+        if (nchunk > 2)
+            issue(2, ra);
+        for (int c = 0; c < nchunk; c += 2) {
+            step(c, rb2);                      // lands c + 1 from rb2, reissues c + 3 there
+            if (c + 1 >= nchunk)
+                break;
+            step(c + 1, ra);                   // lands c + 2 from ra, reissues c + 4 there
         }
     }
 
@@ -1095,23 +1105,19 @@ hipError_t launch_kind(const PartialArgs &a, hipStream_t stream)
         return hipGetLastError();
     }
     const int64_t heads = (int64_t)a.batch * a.kv_heads * a.n_split;
-#define NBX_MULTIROW(RW_, NT_)                                                              \
-    do {                                                                                    \
-        const int rows_per_block = (RW_) * (NT_) * 16;                                      \
-        const int row_blocks = (M + rows_per_block - 1) / rows_per_block;                   \
-        const int64_t blocks = heads * row_blocks;                                          \
-        if (blocks > 0x7FFFFFFF)                                                            \
-            return hipErrorInvalidConfiguration;                                            \
-        hipLaunchKernelGGL((multirow_mfma_kernel<D, KVT, PVS, RW_, NT_>), dim3((unsigned)blocks), \
-                           dim3((RW_) * 64), 0, stream, a, row_blocks);                     \
-    } while (0)
-    if (M % 96 == 0)
-        NBX_MULTIROW(6, 1);
-    else if (M <= 64)
-        NBX_MULTIROW(4, 1);
+    // 8 waves x 16 rows per workgroup; 8 x 32 rows where a KV head has more
+    // rows than one such workgroup holds
+    const int nt = M > 128 ? 2 : 1;
+    const int row_blocks = (M + 128 * nt - 1) / (128 * nt);
+    const int64_t blocks = heads * row_blocks;
+    if (blocks > 0x7FFFFFFF)
+        return hipErrorInvalidConfiguration;
+    if (nt == 2)
+        hipLaunchKernelGGL((multirow_mfma_kernel<D, KVT, PVS, 2>), dim3((unsigned)blocks), dim3(512),
+                           0, stream, a, row_blocks);
     else
-        NBX_MULTIROW(4, 2);
-#undef NBX_MULTIROW
+        hipLaunchKernelGGL((multirow_mfma_kernel<D, KVT, PVS, 1>), dim3((unsigned)blocks), dim3(512),
+                           0, stream, a, row_blocks);
     return hipGetLastError();
 }
 
