@@ -774,6 +774,7 @@ __global__ void __launch_bounds__(512)
 multirow_mfma_kernel(PartialArgs a, int row_blocks)
 {
     constexpr int RW = 8;                      // waves per workgroup
+    constexpr int NSET = 2;                    // register sets of chunks in flight
     constexpr int KK = D / 32, DT = D / 16;
     constexpr bool BF = KVT == NBX_BF16;
     constexpr int ESZ = BF ? 2 : 1;
@@ -782,7 +783,7 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
     constexpr int BUF = KBYTES + VBYTES;
     constexpr int NI = 2 * KK + DT;            // 1 KB (bf16) pieces per chunk: K then V
     constexpr int PER = NI / RW;               // pieces per wave
-    static_assert(NI % RW == 0, "pieces per chunk must split evenly over the waves");
+    static_assert(NI == 4 * KK && NI % RW == 0, "K and V pieces split evenly over the waves");
     constexpr int R = RW * NT * 16;            // rows per workgroup
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF];
 
@@ -861,80 +862,86 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
     const uint8_t *k_rd = smem + (4 * j + ((g + (j >> 2)) & 3)) * 16;   // + (t*KK + kk) * 1024
     const uint8_t *vt_lane = smem + KBYTES + (4 * g + (j >> 2)) * 32 + (j & 3) * 8;
 
-    // page ids of the chunks of even / odd 32-chunk batches (lane i: tile i & 1
-    // of chunk 32 batch + i / 2); two registers, so that refreshing the next
-    // batch keeps the ids of chunks still in flight
-    int pg_even = -1, pg_odd = -1;
-    auto page_of = [&](int c, int t) {
-        const int r = ((c >> 5) & 1) ? pg_odd : pg_even;
-        return __builtin_amdgcn_readlane(r, 2 * (c & 31) + t);
-    };
+    // Wave roles: waves 0-3 load K, 4-7 load V; wave w takes tile (w & 3) / 2
+    // of every chunk and its pieces (w & 1) * PER ... (w & 1) * PER + PER - 1
+    // (K: 32-column groups kk, V: 32-column pairs of 16-column slices).
+    const bool is_k = w < 4;
+    const int t_w = (w & 3) >> 1, pbase = (w & 1) * PER;
+    const uint8_t *role_base = is_k ? (const uint8_t *)a.k_data + k_head * ESZ
+                                    : (const uint8_t *)a.v_data + v_head * ESZ;
+    const int64_t role_sp = (is_k ? a.k_stride_page : a.v_stride_page) * ESZ;
+    const int role_st = is_k ? kst_b : vst_b;
+    const int role_lane = (is_k ? k_lane : v_lane) + pbase * 32 * ESZ;
+
+    // Tiles of the chunks of even / odd 32-chunk batches, lane i holding tile
+    // i & 1 of chunk 32 batch + i / 2: the byte offset of its first row from
+    // this wave's pool and head (lo, hi), the bytes this wave may read from it
+    // (0 for a tile outside the sequence or the pool) and whether it is mapped
+    // (K bytes).  Two sets, so that refreshing the next batch keeps the tiles
+    // of chunks still in flight; filled once per 32 chunks.
+    uint32_t off_lo0 = 0, off_hi0 = 0, nbytes0 = 0, kvalid0 = 0;     // even batches
+    uint32_t off_lo1 = 0, off_hi1 = 0, nbytes1 = 0, kvalid1 = 0;     // odd batches
     auto refresh = [&](int c) {
-        const int v = chunk_pages(a, b, j0, jend, nchunk, c, 1, lane, lead);
-        if ((c >> 5) & 1)
-            pg_odd = v;
-        else
-            pg_even = v;
+        const int page = chunk_pages(a, b, j0, jend, nchunk, c, 1, lane, lead);
+        const int ts = j0 + (c + (lane >> 1)) * kChunk + 16 * (lane & 1);
+        const int row = ts % a.page_tokens;
+        const bool ok = page >= 0;
+        const int64_t off = ok ? (int64_t)page * role_sp + (int64_t)row * role_st : 0;
+        const int vrows = min(16, max(jend - ts, 0));
+        const uint32_t lo = (uint32_t)off, hi = (uint32_t)((uint64_t)off >> 32);
+        const uint32_t nb = ok ? (uint32_t)((is_k ? 16 : vrows) * role_st) : 0u;
+        if ((c >> 5) & 1) {
+            off_lo1 = lo;
+            off_hi1 = hi;
+            nbytes1 = nb;
+            kvalid1 = ok;
+        } else {
+            off_lo0 = lo;
+            off_hi0 = hi;
+            nbytes0 = nb;
+            kvalid0 = ok;
+        }
+    };
+    auto tile_ok = [&](int c, int t) {
+        const uint32_t r = ((c >> 5) & 1) ? kvalid1 : kvalid0;
+        return __builtin_amdgcn_readlane(r, 2 * (c & 31) + t) != 0;
     };
 
     struct Regs {
         u32x4 r16[BF ? PER : 1];
         u32x2 r8[BF ? 1 : PER];
     };
-    // this wave's pieces of chunk c into registers
+    // this wave's pieces of chunk c into registers: one descriptor per chunk
     auto issue = [&](int c, Regs &rg) {
-        const int p0 = j0 + c * kChunk;
-        const int page0 = page_of(c, 0), page1 = page_of(c, 1);
-        const i32x4 rk0 = tile_rsrc<ESZ>(a.k_data, a.k_stride_page, k_head, a.k_stride_token,
-                                         a.page_tokens, page0, p0, 16);
-        const i32x4 rk1 = tile_rsrc<ESZ>(a.k_data, a.k_stride_page, k_head, a.k_stride_token,
-                                         a.page_tokens, page1, p0 + 16, 16);
-        const i32x4 rv0 = tile_rsrc<ESZ>(a.v_data, a.v_stride_page, v_head, a.v_stride_token,
-                                         a.page_tokens, page0, p0, min(16, jend - p0));
-        const i32x4 rv1 = tile_rsrc<ESZ>(a.v_data, a.v_stride_page, v_head, a.v_stride_token,
-                                         a.page_tokens, page1, p0 + 16, min(16, jend - p0 - 16));
+        const int q = (c >> 5) & 1, li = 2 * (c & 31) + t_w;
+        const uint32_t lo = __builtin_amdgcn_readlane(q ? off_lo1 : off_lo0, li);
+        const uint32_t hi = __builtin_amdgcn_readlane(q ? off_hi1 : off_hi0, li);
+        const uint32_t nb = __builtin_amdgcn_readlane(q ? nbytes1 : nbytes0, li);
+        const i32x4 rs = make_buffer_rsrc(role_base + (((uint64_t)hi << 32) | lo), nb);
 #pragma unroll
         for (int x = 0; x < PER; ++x) {
-            const int i = x * RW + w;
-            i32x4 rs;
-            int off;
-            if (i < 2 * KK) {
-                rs = i < KK ? rk0 : rk1;
-                off = k_lane + (i % KK) * 32 * ESZ;
-            } else {
-                const int ii = i - 2 * KK;
-                rs = ii < DT / 2 ? rv0 : rv1;
-                off = v_lane + (ii % (DT / 2)) * 32 * ESZ;
-            }
             if constexpr (BF)
-                rg.r16[x] = nbx_buffer_load_b128(rs, off, 0, 0);
+                rg.r16[x] = nbx_buffer_load_b128(rs, role_lane + x * 32 * ESZ, 0, 0);
             else
-                rg.r8[x] = nbx_buffer_load_b64(rs, off, 0, 0);
+                rg.r8[x] = nbx_buffer_load_b64(rs, role_lane + x * 32 * ESZ, 0, 0);
         }
     };
     // this wave's pieces of a chunk, landed in registers, into an LDS buffer
     // (rows outside a descriptor range were read as zeros)
     auto land = [&](uint8_t *buf, const Regs &rg) {
+        uint8_t *dst = is_k ? buf + (t_w * KK + pbase) * 1024 + k_st
+                            : buf + KBYTES + t_w * DT * 512 + pbase * 1024 + lane * 16;
 #pragma unroll
         for (int x = 0; x < PER; ++x) {
-            const int i = x * RW + w;
-            uint8_t *dst;
-            if (i < 2 * KK) {
-                dst = buf + i * 1024 + k_st;              // piece i = t * KK + kk
-            } else {
-                const int ii = i - 2 * KK;
-                const int t = ii / (DT / 2), k = ii % (DT / 2);
-                dst = buf + KBYTES + t * DT * 512 + k * 1024 + lane * 16;
-            }
             if constexpr (BF)
-                *(u32x4 *)dst = rg.r16[x];
+                *(u32x4 *)(dst + x * 1024) = rg.r16[x];
             else
-                *(u32x4 *)dst = widen8_e4m3(rg.r8[x]);
+                *(u32x4 *)(dst + x * 1024) = widen8_e4m3(rg.r8[x]);
         }
     };
     auto compute = [&](int c, int boff) {
         const int p0 = j0 + c * kChunk;
-        const int page0 = page_of(c, 0), page1 = page_of(c, 1);
+        const bool ok0 = tile_ok(c, 0), ok1 = tile_ok(c, 1);
         f32x4 acc[NT][2];
 #pragma unroll
         for (int n = 0; n < NT; ++n)
@@ -955,7 +962,7 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
             float sc[2][4];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const bool tv = (t ? page1 : page0) >= 0;
+                const bool tv = t ? ok1 : ok0;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int pos = p0 + 16 * t + 4 * g + i;
@@ -977,35 +984,34 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
     };
 
     // Iteration c: barrier (chunk c is in LDS buffer c & 1, every wave is done
-    // with chunk c - 1), compute chunk c, land chunk c + 1 (registers) into
-    // buffer (c + 1) & 1, issue chunk c + 3 into the registers just freed.
-    Regs ra, rb2;
+    // with chunk c - 1), compute chunk c, land chunk c + 1 from registers into
+    // buffer (c + 1) & 1, issue chunk c + 1 + NSET into the registers just
+    // freed (NSET register sets: NSET + 1 chunks ahead of the one computed).
+    // Loads and landings past the last chunk are issued all the same (their
+    // descriptors are empty, so they read zeros and touch no memory): with no
+    // branch around them the waits for each register set stay exact and the
+    // chunks behind it stay in flight.
+    Regs rset[NSET];
     auto step = [&](int c, Regs &land_regs) {
         __syncthreads();
-        if (has_rows)
+        if (has_rows && c < nchunk)
             compute(c, (c & 1) * BUF);
-        if (c + 1 < nchunk) {
-            land(smem + ((c + 1) & 1) * BUF, land_regs);
-            if (c + 3 < nchunk) {
-                if (((c + 3) & 31) == 0)
-                    refresh(c + 3);
-                issue(c + 3, land_regs);
-            }
-        }
+        land(smem + ((c + 1) & 1) * BUF, land_regs);
+        if (((c + 1 + NSET) & 31) == 0)
+            refresh(c + 1 + NSET);
+        issue(c + 1 + NSET, land_regs);
     };
     if (nchunk > 0) {
         refresh(0);
-        issue(0, ra);
-        if (nchunk > 1)
-            issue(1, rb2);
-        land(smem, ra);
-        if (nchunk > 2)
-            issue(2, ra);
-        for (int c = 0; c < nchunk; c += 2) {
-            step(c, rb2);                      // lands c + 1 from rb2, reissues c + 3 there
-            if (c + 1 >= nchunk)
-                break;
-            step(c + 1, ra);                   // lands c + 2 from ra, reissues c + 4 there
+        issue(0, rset[0]);
+        land(smem, rset[0]);
+        issue(1, rset[0]);
+        if constexpr (NSET == 2)
+            issue(2, rset[1]);
+        for (int c = 0; c < nchunk; c += NSET) {
+            step(c, rset[0]);                  // lands c + 1, reissues c + 1 + NSET there
+            if constexpr (NSET == 2)
+                step(c + 1, rset[1]);          // lands c + 2, reissues c + 4 there
         }
     }
 
@@ -1029,6 +1035,7 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
 }
 
 // ------------------------------------------------------------------ dispatch
+
 
 // Waves the current device holds at once for the persistent decode kernel
 // (resident workgroups per CU x CUs), cached per device.
@@ -1106,8 +1113,8 @@ hipError_t launch_kind(const PartialArgs &a, hipStream_t stream)
     }
     const int64_t heads = (int64_t)a.batch * a.kv_heads * a.n_split;
     // 8 waves x 16 rows per workgroup; 8 x 32 rows where a KV head has more
-    // rows than one such workgroup holds
-    const int nt = M > 128 ? 2 : 1;
+    // rows than one such workgroup holds (D = 256 would spill at 32 rows)
+    const int nt = M > 128 && D <= 128 ? 2 : 1;
     const int row_blocks = (M + 128 * nt - 1) / (128 * nt);
     const int64_t blocks = heads * row_blocks;
     if (blocks > 0x7FFFFFFF)

@@ -273,3 +273,36 @@ def test_full_size_against_oracle(workload):
                                case.v_scale, rows=(r0, r1))
         err = max_abs(out[r0:r1], ref[r0:r1])
         assert err <= TOL[case.kv_dtype], (r0, r1, err)
+
+
+# ------------------------------------------------------------------ multi-row shapes
+
+MULTIROW = [
+    # (name, overrides): rows per KV head = GQA group x window rows
+    ("d128_bf16_32rows", dict(batch=3, q_rows=8, causal=True, lens=("uniform", 8, 900),
+                              append=False)),
+    ("d128_bf16_192rows", dict(batch=2, q_rows=48, causal=True, lens=("uniform", 48, 700),
+                               append=False)),
+    ("d64_fp8_24rows", dict(batch=3, head_dim=64, kv_dtype="fp8", q_rows=6, causal=True,
+                            lens=("uniform", 6, 800), append=False)),
+    ("d128_fp8_noncausal_80rows", dict(batch=2, kv_dtype="fp8", q_rows=20, causal=False,
+                                       lens=("uniform", 1, 600), append=False)),
+]
+
+
+@pytest.mark.parametrize("name,over", MULTIROW, ids=[m[0] for m in MULTIROW])
+def test_multirow_shapes_match_oracle(name, over):
+    case = synth.make_case(2, seed=61, **over)
+    print(f"multirow {name} rows/kv={case.q_heads // case.kv_heads * case.q_rows} "
+          f"lens={case.seq_lens.tolist()}", flush=True)
+    dc = DevCase(case)
+    for n_split, split in (dc.plan(), (3, 256)):
+        if n_split * split < int(case.seq_lens.max()):
+            continue
+        out = dc.decode(n_split=n_split, split_size=split)
+        torch.cuda.synchronize()
+        ref, _, _ = _reference(case, dc)
+        assert dc.err_bits() == 0
+        assert torch.isfinite(out).all()
+        err = max_abs(out, ref)
+        assert err <= TOL[case.kv_dtype], (n_split, split, err)
