@@ -130,6 +130,55 @@ __device__ __forceinline__ u32x4 vt_operand(const uint8_t *lane_base, int dt)
     return u32x4{ua[0], ua[1], ub[0], ub[1]};
 }
 
+// Online-softmax step for one lane's row over NK k-steps of 32 positions (two
+// 16-position tiles each): sc holds the scaled scores (log2 units, -inf where
+// masked).  Updates m, l, rescales o and returns the P operands of the k-steps
+// (hi and residual lo parts).
+template <int DT, bool PVS, int NK>
+__device__ __forceinline__ void softmax_step_n(float (&sc)[2 * NK][4], float &m_run, float &l_run,
+                                               f32x4 (&o)[DT], u32x4 (&ph)[NK], u32x4 (&pl)[NK])
+{
+    float mx = sc[0][0];
+#pragma unroll
+    for (int t = 0; t < 2 * NK; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            mx = fmaxf(mx, sc[t][i]);
+    mx = xor_max16_32(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_safe = m_new == -INFINITY ? 0.0f : m_new;
+    const float corr = fast_exp2(m_run - m_safe);
+    float p[2 * NK][4], psum = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 2 * NK; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[t][i] = fast_exp2(sc[t][i] - m_safe);
+            psum += p[t][i];
+        }
+    l_run = l_run * corr + psum;
+    m_run = m_new;
+    if (__any(corr != 1.0f)) {             // a row's max moved: rescale (else o * 1 = o)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+            o[dt] *= corr;
+    }
+#pragma unroll
+    for (int k = 0; k < NK; ++k)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int t = 2 * k + u;
+            ph[k][2 * u] = pack_bf16(p[t][0], p[t][1]);
+            ph[k][2 * u + 1] = pack_bf16(p[t][2], p[t][3]);
+            if constexpr (PVS) {
+                pl[k][2 * u] =
+                    pack_bf16(p[t][0] - bf16_round(p[t][0]), p[t][1] - bf16_round(p[t][1]));
+                pl[k][2 * u + 1] =
+                    pack_bf16(p[t][2] - bf16_round(p[t][2]), p[t][3] - bf16_round(p[t][3]));
+            }
+        }
+}
+
 // Online-softmax step for one lane's row over the 32 positions of a chunk:
 // sc holds the scaled scores (log2 units, -inf where masked).  Updates m, l,
 // rescales o and returns the P operand (hi and residual lo parts).
@@ -769,21 +818,23 @@ decode_persistent_kernel(PartialArgs a)
 // per chunk.  K is stored in LDS with a 16-byte swizzle inside each 1 KB
 // block (row r, piece p at unit 4 r + ((p + r / 4) & 3)), so that the 16
 // lanes of a group reading one 16-byte operand piece each cover all banks.
-template <int D, int KVT, bool PVS, int NT>
+template <int D, int KVT, bool PVS, int NT, int NK, int NSET>
 __global__ void __launch_bounds__(512)
 multirow_mfma_kernel(PartialArgs a, int row_blocks)
 {
     constexpr int RW = 8;                      // waves per workgroup
-    constexpr int NSET = 2;                    // register sets of chunks in flight
+    constexpr int CH = 32 * NK;                // positions per chunk (NK k-steps of P V)
+    constexpr int TL = 2 * NK;                 // 16-position tiles per chunk
+    constexpr int BATCH = 64 / TL;             // chunks whose tiles fill one lane register
     constexpr int KK = D / 32, DT = D / 16;
     constexpr bool BF = KVT == NBX_BF16;
     constexpr int ESZ = BF ? 2 : 1;
-    constexpr int KBYTES = kChunk * 2 * D;     // K chunk as bf16: [tile][KK][16 rows][64 B]
-    constexpr int VBYTES = kChunk * 2 * D;     // V chunk as bf16: [tile][DT][16 rows][32 B]
+    constexpr int KBYTES = CH * 2 * D;         // K chunk as bf16: [tile][KK][16 rows][64 B]
+    constexpr int VBYTES = CH * 2 * D;         // V chunk as bf16: [tile][DT][16 rows][32 B]
     constexpr int BUF = KBYTES + VBYTES;
-    constexpr int NI = 2 * KK + DT;            // 1 KB (bf16) pieces per chunk: K then V
+    constexpr int NI = TL * 2 * KK;            // 1 KB (bf16) pieces per chunk: K then V
     constexpr int PER = NI / RW;               // pieces per wave
-    static_assert(NI == 4 * KK && NI % RW == 0, "K and V pieces split evenly over the waves");
+    static_assert(PER <= KK && KK % PER == 0, "a wave's pieces lie in one tile");
     constexpr int R = RW * NT * 16;            // rows per workgroup
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF];
 
@@ -826,7 +877,7 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
     }
     const int j0 = s * a.split_size;
     const int jend = min(j0 + a.split_size, n_max);
-    const int nchunk = jend > j0 ? (jend - j0 + kChunk - 1) / kChunk : 0;
+    const int nchunk = jend > j0 ? (jend - j0 + CH - 1) / CH : 0;
 
     u32x4 qb[NT][KK];
 #pragma unroll
@@ -862,35 +913,37 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
     const uint8_t *k_rd = smem + (4 * j + ((g + (j >> 2)) & 3)) * 16;   // + (t*KK + kk) * 1024
     const uint8_t *vt_lane = smem + KBYTES + (4 * g + (j >> 2)) * 32 + (j & 3) * 8;
 
-    // Wave roles: waves 0-3 load K, 4-7 load V; wave w takes tile (w & 3) / 2
-    // of every chunk and its pieces (w & 1) * PER ... (w & 1) * PER + PER - 1
-    // (K: 32-column groups kk, V: 32-column pairs of 16-column slices).
+    // Wave roles: waves 0-3 load K, 4-7 load V; of the TL x KK pieces of its
+    // pool (tile-major: K 32-column groups kk, V 32-column pairs of 16-column
+    // slices) wave w takes (w & 3) * PER ... (w & 3) * PER + PER - 1, all in
+    // tile t_w of every chunk.
     const bool is_k = w < 4;
-    const int t_w = (w & 3) >> 1, pbase = (w & 1) * PER;
+    const int t_w = ((w & 3) * PER) / KK, pbase = ((w & 3) * PER) % KK;
     const uint8_t *role_base = is_k ? (const uint8_t *)a.k_data + k_head * ESZ
                                     : (const uint8_t *)a.v_data + v_head * ESZ;
     const int64_t role_sp = (is_k ? a.k_stride_page : a.v_stride_page) * ESZ;
     const int role_st = is_k ? kst_b : vst_b;
     const int role_lane = (is_k ? k_lane : v_lane) + pbase * 32 * ESZ;
 
-    // Tiles of the chunks of even / odd 32-chunk batches, lane i holding tile
-    // i & 1 of chunk 32 batch + i / 2: the byte offset of its first row from
+    // Tiles of the chunks of even / odd batches of BATCH chunks, lane i holding
+    // tile i % TL of chunk BATCH batch + i / TL: the byte offset of its first row from
     // this wave's pool and head (lo, hi), the bytes this wave may read from it
     // (0 for a tile outside the sequence or the pool) and whether it is mapped
     // (K bytes).  Two sets, so that refreshing the next batch keeps the tiles
-    // of chunks still in flight; filled once per 32 chunks.
+    // of chunks still in flight; filled once per batch.
     uint32_t off_lo0 = 0, off_hi0 = 0, nbytes0 = 0, kvalid0 = 0;     // even batches
     uint32_t off_lo1 = 0, off_hi1 = 0, nbytes1 = 0, kvalid1 = 0;     // odd batches
     auto refresh = [&](int c) {
-        const int page = chunk_pages(a, b, j0, jend, nchunk, c, 1, lane, lead);
-        const int ts = j0 + (c + (lane >> 1)) * kChunk + 16 * (lane & 1);
+        const int cq = c + lane / TL;
+        const int ts = j0 + cq * CH + 16 * (lane % TL);
+        const int page = cq < nchunk ? tile_page(a, b, ts, jend, lead) : -1;
         const int row = ts % a.page_tokens;
         const bool ok = page >= 0;
         const int64_t off = ok ? (int64_t)page * role_sp + (int64_t)row * role_st : 0;
         const int vrows = min(16, max(jend - ts, 0));
         const uint32_t lo = (uint32_t)off, hi = (uint32_t)((uint64_t)off >> 32);
         const uint32_t nb = ok ? (uint32_t)((is_k ? 16 : vrows) * role_st) : 0u;
-        if ((c >> 5) & 1) {
+        if ((c / BATCH) & 1) {
             off_lo1 = lo;
             off_hi1 = hi;
             nbytes1 = nb;
@@ -903,8 +956,8 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
         }
     };
     auto tile_ok = [&](int c, int t) {
-        const uint32_t r = ((c >> 5) & 1) ? kvalid1 : kvalid0;
-        return __builtin_amdgcn_readlane(r, 2 * (c & 31) + t) != 0;
+        const uint32_t r = ((c / BATCH) & 1) ? kvalid1 : kvalid0;
+        return __builtin_amdgcn_readlane(r, TL * (c % BATCH) + t) != 0;
     };
 
     struct Regs {
@@ -913,7 +966,7 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
     };
     // this wave's pieces of chunk c into registers: one descriptor per chunk
     auto issue = [&](int c, Regs &rg) {
-        const int q = (c >> 5) & 1, li = 2 * (c & 31) + t_w;
+        const int q = (c / BATCH) & 1, li = TL * (c % BATCH) + t_w;
         const uint32_t lo = __builtin_amdgcn_readlane(q ? off_lo1 : off_lo0, li);
         const uint32_t hi = __builtin_amdgcn_readlane(q ? off_hi1 : off_hi0, li);
         const uint32_t nb = __builtin_amdgcn_readlane(q ? nbytes1 : nbytes0, li);
@@ -940,47 +993,53 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
         }
     };
     auto compute = [&](int c, int boff) {
-        const int p0 = j0 + c * kChunk;
-        const bool ok0 = tile_ok(c, 0), ok1 = tile_ok(c, 1);
-        f32x4 acc[NT][2];
+        const int p0 = j0 + c * CH;
+        bool ok[TL];
+#pragma unroll
+        for (int t = 0; t < TL; ++t)
+            ok[t] = tile_ok(c, t);
+        f32x4 acc[NT][TL];
 #pragma unroll
         for (int n = 0; n < NT; ++n)
-            acc[n][0] = acc[n][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < TL; ++t)
+                acc[n][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
+        for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+            for (int t = 0; t < TL; ++t) {
                 const u32x4 ka = *(const u32x4 *)(k_rd + boff + (t * KK + kk) * 1024);
 #pragma unroll
                 for (int n = 0; n < NT; ++n)
                     acc[n][t] = mfma_bf16(ka, qb[n][kk], acc[n][t]);
             }
-        u32x4 ph[NT], pl[NT];
+        u32x4 ph[NT][NK], pl[NT][NK];
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
             const int e_n = min(jend, n_row[n]);
-            float sc[2][4];
+            float sc[TL][4];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const bool tv = t ? ok1 : ok0;
+            for (int t = 0; t < TL; ++t) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int pos = p0 + 16 * t + 4 * g + i;
-                    sc[t][i] = (tv && pos < e_n) ? acc[n][t][i] * scale2 : -INFINITY;
+                    sc[t][i] = (ok[t] && pos < e_n) ? acc[n][t][i] * scale2 : -INFINITY;
                 }
             }
-            softmax_step<DT, PVS>(sc, m_run[n], l_run[n], o[n], ph[n], pl[n]);
+            softmax_step_n<DT, PVS, NK>(sc, m_run[n], l_run[n], o[n], ph[n], pl[n]);
         }
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            const u32x4 va = vt_operand<DT>(vt_lane + boff, dt);
+        for (int kq = 0; kq < NK; ++kq)
 #pragma unroll
-            for (int n = 0; n < NT; ++n) {
-                o[n][dt] = mfma_bf16(va, ph[n], o[n][dt]);
-                if constexpr (PVS)
-                    o[n][dt] = mfma_bf16(va, pl[n], o[n][dt]);
+            for (int dt = 0; dt < DT; ++dt) {
+                const u32x4 va = vt_operand<DT>(vt_lane + boff + kq * 2 * DT * 512, dt);
+#pragma unroll
+                for (int n = 0; n < NT; ++n) {
+                    o[n][dt] = mfma_bf16(va, ph[n][kq], o[n][dt]);
+                    if constexpr (PVS)
+                        o[n][dt] = mfma_bf16(va, pl[n][kq], o[n][dt]);
+                }
             }
-        }
     };
 
     // Iteration c: barrier (chunk c is in LDS buffer c & 1, every wave is done
@@ -997,7 +1056,7 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
         if (has_rows && c < nchunk)
             compute(c, (c & 1) * BUF);
         land(smem + ((c + 1) & 1) * BUF, land_regs);
-        if (((c + 1 + NSET) & 31) == 0)
+        if ((c + 1 + NSET) % BATCH == 0)
             refresh(c + 1 + NSET);
         issue(c + 1 + NSET, land_regs);
     };
@@ -1035,6 +1094,9 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
 }
 
 // ------------------------------------------------------------------ dispatch
+
+// multi-row chunks: 2 k-steps (64 positions), one register set in flight
+constexpr int kMrNK = 2, kMrNSet = 1;
 
 
 // Waves the current device holds at once for the persistent decode kernel
@@ -1112,19 +1174,19 @@ hipError_t launch_kind(const PartialArgs &a, hipStream_t stream)
         return hipGetLastError();
     }
     const int64_t heads = (int64_t)a.batch * a.kv_heads * a.n_split;
-    // 8 waves x 16 rows per workgroup; 8 x 32 rows where a KV head has more
-    // rows than one such workgroup holds (D = 256 would spill at 32 rows)
+    // 8 waves x 16 rows per workgroup (8 x 32 where a KV head has more rows
+    // than that and D <= 128: D = 256 would spill at 32 rows per wave)
     const int nt = M > 128 && D <= 128 ? 2 : 1;
     const int row_blocks = (M + 128 * nt - 1) / (128 * nt);
     const int64_t blocks = heads * row_blocks;
     if (blocks > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
     if (nt == 2)
-        hipLaunchKernelGGL((multirow_mfma_kernel<D, KVT, PVS, 2>), dim3((unsigned)blocks), dim3(512),
-                           0, stream, a, row_blocks);
+        hipLaunchKernelGGL((multirow_mfma_kernel<D, KVT, PVS, 2, kMrNK, kMrNSet>),
+                           dim3((unsigned)blocks), dim3(512), 0, stream, a, row_blocks);
     else
-        hipLaunchKernelGGL((multirow_mfma_kernel<D, KVT, PVS, 1>), dim3((unsigned)blocks), dim3(512),
-                           0, stream, a, row_blocks);
+        hipLaunchKernelGGL((multirow_mfma_kernel<D, KVT, PVS, 1, kMrNK, kMrNSet>),
+                           dim3((unsigned)blocks), dim3(512), 0, stream, a, row_blocks);
     return hipGetLastError();
 }
 
