@@ -152,6 +152,11 @@ size_t nbx_paged_decode_workspace_bytes(int64_t rows, int32_t n_split, int32_t h
  *                row sees.  split_size * n_split must cover every sequence
  *                (not checkable on the host: longer sequences set
  *                NBX_DEVERR_SEQ_RANGE and their tail is not read).
+ *                split_size == 0: derived on the device at every launch from
+ *                the lengths, ceil(ceil(max(longest, 1) / n_split) / 16) * 16
+ *                (the split kernel's rule on the nbxtensor paged_decode_attn.py
+ *                page), so a launch recorded in a graph stays right as the
+ *                lengths grow; n_split then only bounds the split count.
  *   o_part       device fp32 [rows, n_split, head_dim]: sum_j exp(s_j - m) v_j
  *   m_part       device fp32 [rows, n_split]: max_j s_j (natural-log units)
  *   l_part       device fp32 [rows, n_split]: sum_j exp(s_j - m)
@@ -244,6 +249,15 @@ int nbx_paged_decode_step(const void *q, int32_t q_dtype, int32_t batch, int32_t
                           int32_t split_size, int32_t n_split, void *workspace,
                           size_t workspace_bytes, void *out, int32_t out_dtype, int32_t *dev_err,
                           hipStream_t stream);
+
+/*
+ * nbx_paged_lens_advance - seq_lens[b] += n for 0 <= b < batch, on the device
+ * (nbxtensor paged_decode_attn.py, paged_lens_advance_kernel: the length of a
+ * decode step moves on the device, so a recorded step replays unchanged).
+ *   seq_lens  device int32 [batch].  batch == 0 is a no-op; batch < 0 gives
+ *             NBX_ERR_BAD_SHAPE.  Overflow of an int32 length is the caller's.
+ */
+int nbx_paged_lens_advance(int32_t *seq_lens, int32_t batch, int32_t n, hipStream_t stream);
 
 /* nbx_status_str - static message text for a status code (never null). */
 const char *nbx_status_str(int status);

@@ -81,6 +81,8 @@ def load_library():
                                                   PP, P, I32, P, F, I32, I32, P, ctypes.c_size_t,
                                                   P, I32, P, P]
             lib.nbx_paged_decode_step.restype = ctypes.c_int
+            lib.nbx_paged_lens_advance.argtypes = [P, I32, I32, P]
+            lib.nbx_paged_lens_advance.restype = ctypes.c_int
             lib.nbx_status_str.argtypes = [ctypes.c_int]
             lib.nbx_status_str.restype = ctypes.c_char_p
             lib.nbx_version.restype = ctypes.c_int
@@ -281,3 +283,12 @@ def workspace_partials(workspace, rows: int, n_split: int, head_dim: int):
     off = r256(o_b) + r256(ml_b)
     l = workspace[off:off + ml_b].view(torch.float32).view(rows, n_split)
     return o, m, l
+
+
+def nbx_paged_lens_advance(seq_lens, n: int, stream=None):
+    """seq_lens[b] += n on the device (int32 device tensor)."""
+    if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 tensor")
+    st = load_library().nbx_paged_lens_advance(_ptr(seq_lens), int(seq_lens.numel()), int(n),
+                                               _stream(stream))
+    _check(st, "nbx_paged_lens_advance")

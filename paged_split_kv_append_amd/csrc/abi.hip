@@ -101,6 +101,15 @@ size_t nbx_paged_decode_workspace_bytes(int64_t rows, int32_t n_split, int32_t h
     return round256(o) + 2 * round256(ml);
 }
 
+int nbx_paged_lens_advance(int32_t *seq_lens, int32_t batch, int32_t n, hipStream_t stream)
+{
+    if (!seq_lens)
+        return NBX_ERR_NULL_PTR;
+    if (batch < 0)
+        return NBX_ERR_BAD_SHAPE;
+    return to_status(nbx::launch_lens_advance(seq_lens, batch, n, stream));
+}
+
 int nbx_paged_kv_append(const void *new_k, const void *new_v, int32_t new_dtype, int64_t n_tok,
                         int64_t new_stride_tok, int64_t new_stride_head,
                         const nbx_kv_pool *k_pool, const nbx_kv_pool *v_pool,
@@ -183,7 +192,7 @@ static int validate_partial(const void *q, int32_t q_dtype, int32_t batch, int32
         return NBX_ERR_BAD_SHAPE;
     if (scale != scale || scale == INFINITY || scale == -INFINITY)
         return NBX_ERR_BAD_SHAPE;
-    if (split_size < 16 || split_size % 16)
+    if (split_size < 0 || split_size % 16)   // 0: derived on the device from seq_lens
         return NBX_ERR_BAD_ALIGN;
     if (n_split < 1 || n_split > kMaxGridYZ)
         return NBX_ERR_BAD_SHAPE;

@@ -132,6 +132,26 @@ static hipError_t launch_append_t(const AppendArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
+// seq_lens[b] += n for every sequence (nbxtensor paged_decode_attn.py,
+// paged_lens_advance_kernel: the length moves on the device after the step's
+// append, so a recorded step replays with the same arguments)
+__global__ void __launch_bounds__(256)
+lens_advance_kernel(int32_t *seq_lens, int32_t batch, int32_t n)
+{
+    const int b = blockIdx.x * 256 + threadIdx.x;
+    if (b < batch)
+        seq_lens[b] += n;
+}
+
+hipError_t launch_lens_advance(int32_t *seq_lens, int32_t batch, int32_t n, hipStream_t stream)
+{
+    if (batch <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(lens_advance_kernel, dim3((unsigned)((batch + 255) / 256)), dim3(256), 0,
+                       stream, seq_lens, batch, n);
+    return hipGetLastError();
+}
+
 hipError_t launch_append(const AppendArgs &a, hipStream_t stream)
 {
     if (a.src_dtype == NBX_F32) {

@@ -53,6 +53,25 @@ struct PartialArgs {
     int32_t new_dtype, n_new;
 };
 
+// Positions per split: the caller's, or with split_size == 0 the rule of the
+// nbxtensor paged_decode_attn.py split kernel evaluated on the device lengths,
+// ceil(ceil(max(longest, 1) / n_split) / 16) * 16, so that a recorded launch
+// stays right as the lengths grow (lengths clamped to the block-table row).
+__device__ inline int device_split_size(const PartialArgs &a)
+{
+    if (a.split_size > 0)
+        return a.split_size;
+    const int cap = a.max_pages * a.page_tokens;
+    int longest = 1;
+    for (int b = 0; b < a.batch; ++b) {
+        int L = a.seq_lens[b];
+        L = L < 0 ? 0 : (L > cap ? cap : L);
+        longest = L > longest ? L : longest;
+    }
+    const int per = (longest + a.n_split - 1) / a.n_split;
+    return (per + 15) / 16 * 16;
+}
+
 struct MergeArgs {
     const float *o_part, *m_part, *l_part;
     int64_t rows;
@@ -62,6 +81,7 @@ struct MergeArgs {
 };
 
 hipError_t launch_append(const AppendArgs &a, hipStream_t stream);
+hipError_t launch_lens_advance(int32_t *seq_lens, int32_t batch, int32_t n, hipStream_t stream);
 hipError_t launch_partial_valu(const PartialArgs &a, hipStream_t stream);
 hipError_t launch_partial_mfma(const PartialArgs &a, hipStream_t stream);
 // true when launch_partial_mfma runs `a` as one persistent launch, so that it

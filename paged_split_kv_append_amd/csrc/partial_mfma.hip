@@ -252,8 +252,9 @@ decode_mfma_kernel(PartialArgs a)
     const int64_t row_base = ((int64_t)b * a.q_heads + (int64_t)gk * a.group) * a.q_rows;
     const bool lead = threadIdx.x == 0;
 
+    const int S = device_split_size(a);
     const int L = clamp_len(a, b, lead && s == 0);
-    if (lead && s == a.n_split - 1 && L > a.n_split * a.split_size)
+    if (lead && s == a.n_split - 1 && L > a.n_split * S)
         flag_error(a.dev_err, NBX_DEVERR_SEQ_RANGE);
 
     int n_j = 0;
@@ -263,8 +264,8 @@ decode_mfma_kernel(PartialArgs a)
     }
     int n_max = a.causal ? L - a.q_rows + min(M, a.q_rows) : L;
     n_max = n_max < 0 ? 0 : n_max;
-    const int j0 = s * a.split_size;
-    const int jend = min(j0 + a.split_size, n_max);
+    const int j0 = s * S;
+    const int jend = min(j0 + S, n_max);
     const int e_j = min(jend, n_j);
     const int nchunk = jend > j0 ? (jend - j0 + kChunk - 1) / kChunk : 0;
 
@@ -505,13 +506,13 @@ decode_persistent_kernel(PartialArgs a)
     const int lane = threadIdx.x;
     const int g = lane >> 4, j = lane & 15;
     const int wv = blockIdx.x, W = gridDim.x;
-    const int M = a.rows_per_kv, S = a.split_size, H = a.kv_heads, NS = a.n_split;
+    const int M = a.rows_per_kv, H = a.kv_heads, NS = a.n_split;
     const int cap = a.max_pages * a.page_tokens;
 
     // sequence table, lane l of block t describing b = 64 t + l: clamped
     // length, splits holding keys, inclusive prefix of item counts
     int Lr[NB], nsr[NB], incl[NB];
-    int carry = 0;
+    int longest = 1;
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
         const int b = 64 * t + lane;
@@ -523,9 +524,26 @@ decode_persistent_kernel(PartialArgs a)
                     flag_error(a.dev_err, NBX_DEVERR_SEQ_RANGE);
                 L = L < 0 ? 0 : cap;
             }
-            if (wv == 0 && (L > NS * S || (FA && L < a.n_new)))
-                flag_error(a.dev_err, NBX_DEVERR_SEQ_RANGE);
         }
+        Lr[t] = L;
+        longest = max(longest, L);
+    }
+    // positions per split: the caller's, or (split_size == 0) derived from the
+    // longest device length as device_split_size does
+    int S = a.split_size;
+    if (S == 0) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1)
+            longest = max(longest, __shfl_xor(longest, off, 64));
+        S = ((longest + NS - 1) / NS + 15) / 16 * 16;
+    }
+    int carry = 0;
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+        const int b = 64 * t + lane;
+        const int L = Lr[t];
+        if (wv == 0 && b < a.batch && (L > NS * S || (FA && L < a.n_new)))
+            flag_error(a.dev_err, NBX_DEVERR_SEQ_RANGE);
         int nmax = a.causal ? L - a.q_rows + min(M, a.q_rows) : L;
         nmax = nmax < 0 ? 0 : nmax;
         const int ns = b < a.batch ? min((nmax + S - 1) / S, NS) : 0;
@@ -536,7 +554,6 @@ decode_persistent_kernel(PartialArgs a)
             if (lane >= off)
                 x += y;
         }
-        Lr[t] = L;
         nsr[t] = ns;
         incl[t] = carry + x;
         carry = __shfl(incl[t], 63, 64);
@@ -854,8 +871,9 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
     // a wave whose row tiles are all past the last row loads its share only
     const bool has_rows = row_lo + w * NT * 16 < row_hi;
 
+    const int S = device_split_size(a);
     const int L = clamp_len(a, b, lead && s == 0 && rb == 0);
-    if (lead && rb == 0 && s == a.n_split - 1 && L > a.n_split * a.split_size)
+    if (lead && rb == 0 && s == a.n_split - 1 && L > a.n_split * S)
         flag_error(a.dev_err, NBX_DEVERR_SEQ_RANGE);
 
     int n_row[NT];
@@ -875,8 +893,8 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
         for (int m = row_lo; m < row_hi && m < row_lo + a.q_rows; ++m)
             n_max = max(n_max, L - a.q_rows + (m % a.q_rows) + 1);
     }
-    const int j0 = s * a.split_size;
-    const int jend = min(j0 + a.split_size, n_max);
+    const int j0 = s * S;
+    const int jend = min(j0 + S, n_max);
     const int nchunk = jend > j0 ? (jend - j0 + CH - 1) / CH : 0;
 
     u32x4 qb[NT][KK];
@@ -1160,7 +1178,9 @@ hipError_t launch_kind(const PartialArgs &a, hipStream_t stream)
         return hipErrorInvalidValue;           // the caller appends first for these shapes
     if (M <= 16) {
         // waves per (split, head): enough that each wave's run of chunks is short
-        const int chunks = (a.split_size + kChunk - 1) / kChunk;
+        const int split = a.split_size > 0 ? a.split_size
+                                           : (a.max_pages * a.page_tokens + a.n_split - 1) / a.n_split;
+        const int chunks = (split + kChunk - 1) / kChunk;
         const int64_t blocks = (int64_t)a.n_split * a.batch * a.kv_heads;
         if (blocks > 0x7FFFFFFF)
             return hipErrorInvalidConfiguration;

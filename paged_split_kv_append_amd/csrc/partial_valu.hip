@@ -56,6 +56,7 @@ partial_valu_kernel(PartialArgs a)
     const int rows_here = min(RB, a.rows_per_kv - row0);
     const int64_t row_base = ((int64_t)b * a.q_heads + (int64_t)g * a.group) * a.q_rows;
 
+    const int S = device_split_size(a);
     int L = a.seq_lens[b];
     const int cap = a.max_pages * a.page_tokens;
     if (L < 0 || L > cap) {
@@ -63,7 +64,7 @@ partial_valu_kernel(PartialArgs a)
             flag_error(a.dev_err, NBX_DEVERR_SEQ_RANGE);
         L = L < 0 ? 0 : cap;
     }
-    if (s == a.n_split - 1 && L > a.n_split * a.split_size && t == 0 && rb == 0)
+    if (s == a.n_split - 1 && L > a.n_split * S && t == 0 && rb == 0)
         flag_error(a.dev_err, NBX_DEVERR_SEQ_RANGE);
 
     for (int idx = t; idx < RB * D; idx += kThreads) {
@@ -87,8 +88,8 @@ partial_valu_kernel(PartialArgs a)
 #pragma unroll
     for (int i = 0; i < RB; ++i)
         n_max = max(n_max, n_s[i]);
-    const int j_begin = s * a.split_size;
-    const int j_end = min(j_begin + a.split_size, n_max);
+    const int j_begin = s * S;
+    const int j_end = min(j_begin + S, n_max);
     const float scale2 = a.scale * a.k_scale * kLog2e;
 
     const int e_c = t % D, pg = t / D;

@@ -19,7 +19,8 @@ def test_every_declared_symbol_is_exported(lib):
     names = nb.declared_symbols()
     assert {"nbx_paged_kv_append", "nbx_paged_decode_partial", "nbx_paged_decode_merge",
             "nbx_paged_decode", "nbx_paged_decode_plan", "nbx_paged_decode_workspace_bytes",
-            "nbx_status_str", "nbx_version"} <= set(names)
+            "nbx_status_str", "nbx_version", "nbx_paged_decode_step",
+            "nbx_paged_lens_advance"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -83,7 +84,7 @@ def partial_status(lib, k=None, v=None, q_dtype=1, batch=2, q_heads=4, q_rows=1,
     (dict(q_heads=3), -3),
     (dict(k=pool(kv_heads=4)), -3),
     (dict(k=pool(page_tokens=8)), -4), (dict(k=pool(page_tokens=24)), -4),
-    (dict(split=100), -4), (dict(split=0), -4),
+    (dict(split=100), -4), (dict(split=-16), -4),
     (dict(n_split=0), -3),
     (dict(k=pool(stride_token=136)), -4),
     (dict(k=pool(data=FAKE + 8)), -4),
@@ -154,3 +155,9 @@ def test_step_validation(lib):
     assert call(ws=None) == -5
     assert call(nbytes=need - 1) == -5
     assert call(ws=FAKE + 16) == -5
+
+
+def test_lens_advance_validation(lib):
+    assert lib.nbx_paged_lens_advance(None, 4, 1, None) == -1
+    assert lib.nbx_paged_lens_advance(FAKE, -1, 1, None) == -3
+    assert lib.nbx_paged_lens_advance(FAKE, 0, 1, None) == 0      # nothing launched

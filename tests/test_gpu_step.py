@@ -228,3 +228,88 @@ def test_step_bf16_output():
     err = np.abs(out.double().cpu().numpy().reshape(ref.shape) - ref)
     half_ulp = np.abs(ref) * 2.0 ** -8
     assert np.all(err <= TOL["bf16"] + half_ulp)
+
+
+# ------------------------------------------------------------------ device-side plan and graph replay
+
+@pytest.mark.parametrize("workload", [1, 2, 3, 5])
+def test_device_derived_split_equals_host_plan(workload):
+    """split_size = 0 derives the split length from the device lengths by the
+    plan's own rule, so the partials are bitwise those of the host plan."""
+    over = {1: dict(), 2: dict(batch=6, lens=("uniform", 1, 700)),
+            3: dict(batch=2, lens=("uniform", 300, 900)),
+            5: dict(batch=3, lens=("loguniform", 100, 3000))}[workload]
+    case = synth.make_case(workload, seed=72, append=False, **over)
+    dc = DevCase(case)
+    n_split, split = dc.plan()
+    o1, m1, l1 = dc.partial(n_split, split)
+    o2, m2, l2 = dc.partial(n_split, 0)
+    torch.cuda.synchronize()
+    assert dc.err_bits() == 0
+    assert torch.equal(m1, m2) and torch.equal(l1, l2)
+    keep = torch.isfinite(m1)                  # an empty split's o is left unwritten
+    assert torch.equal(o1[keep], o2[keep])
+
+
+def test_lens_advance():
+    lens = torch.tensor([0, 5, 100, 7], dtype=torch.int32, device="cuda")
+    nb.nbx_paged_lens_advance(lens, 3)
+    torch.cuda.synchronize()
+    assert lens.tolist() == [3, 8, 103, 10]
+
+
+def test_step_graph_replays_as_lengths_grow():
+    """One recorded graph of [lens advance, step with a device-derived split]
+    replayed for four tokens: every replay appends at the new last position and
+    attends to it, with the launch arguments unchanged."""
+    steps = 4
+    case = synth.make_case(2, seed=71, append=False, batch=5, lens=("uniform", 40, 600))
+    final = case.seq_lens.copy()
+    start = final - steps
+    T = case.page_tokens
+    slots = [np.array([int(case.block_table[b, p // T]) * T + p % T
+                       for b, p in enumerate(start + k)], dtype=np.int32) for k in range(steps)]
+    _poison_slots(case, np.concatenate(slots))
+    n_split, _ = nb.nbx_paged_decode_plan(int(final.max()), 256, 64)
+    H, D = case.kv_heads, case.head_dim
+
+    # warm-up on a copy (fills the library's per-device launch cache)
+    warm = DevCase(case)
+    warm.lens.copy_(torch.from_numpy(start + 1))
+    warm.step(torch.zeros(case.batch, 1, H, D, device="cuda"),
+              torch.zeros(case.batch, 1, H, D, device="cuda"), n_split=n_split, split_size=0)
+    torch.cuda.synchronize()
+
+    dc = DevCase(case)
+    dc.lens.copy_(torch.from_numpy(start))
+    kp, vp = dc.pools()
+    ws = torch.zeros(nb.nbx_paged_decode_workspace_bytes(case.rows, n_split, D),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty(case.batch, case.q_heads, 1, D, device="cuda")
+    nk = torch.zeros(case.batch, 1, H, D, device="cuda")
+    nv = torch.zeros_like(nk)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        nb.nbx_paged_lens_advance(dc.lens, 1)
+        nb.nbx_paged_decode_step(dc.q, kp, vp, dc.bt, dc.lens, case.softmax_scale, 0, n_split, ws,
+                                 out, new_k=nk, new_v=nv, dev_err=dc.err)
+    gen = torch.Generator().manual_seed(71)
+    k_ref, v_ref = case.k_pool, case.v_pool
+    for k in range(steps):
+        tok_k = torch.randn(case.batch, 1, H, D, generator=gen)
+        tok_v = torch.randn(case.batch, 1, H, D, generator=gen)
+        nk.copy_(tok_k)
+        nv.copy_(tok_v)
+        g.replay()
+        torch.cuda.synchronize()
+        k_ref, _ = oracle.append(tok_k.reshape(-1, H, D), "f32", k_ref, case.kv_dtype, 1.0, T, slots[k])
+        v_ref, _ = oracle.append(tok_v.reshape(-1, H, D), "f32", v_ref, case.kv_dtype, 1.0, T, slots[k])
+        lens_k = (start + k + 1).astype(np.int32)
+        assert dc.lens.cpu().numpy().tolist() == lens_k.tolist()
+        ref = oracle.attention(case.q, case.q_dtype, k_ref, v_ref, case.kv_dtype,
+                               case.block_table, lens_k, case.softmax_scale)
+        print(f"replay {k}: lens {lens_k.tolist()}", flush=True)
+        assert dc.err_bits() == 0
+        assert torch.isfinite(out).all()
+        assert max_abs(out.reshape(case.rows, D), ref) <= TOL["bf16"]
