@@ -306,3 +306,25 @@ def test_multirow_shapes_match_oracle(name, over):
         assert torch.isfinite(out).all()
         err = max_abs(out, ref)
         assert err <= TOL[case.kv_dtype], (n_split, split, err)
+
+
+# ------------------------------------------------------------------ other page sizes
+
+@pytest.mark.parametrize("workload,page_tokens", [(2, 48), (2, 128), (3, 48), (4, 80), (5, 64)])
+def test_page_sizes_match_oracle(workload, page_tokens):
+    """Pages of 48, 64, 80 and 128 positions: tiles start at non-zero rows of a
+    page, and a split may start mid-page."""
+    over = {2: dict(batch=5, lens=("uniform", 1, 900)), 3: dict(batch=2, lens=("uniform", 300, 900)),
+            4: dict(lens=("fixed", 700)), 5: dict(batch=3, lens=("loguniform", 100, 3000))}[workload]
+    case = synth.make_case(workload, seed=81, page_tokens=page_tokens, **over)
+    print(f"pages of {page_tokens}: workload {workload} lens={case.seq_lens.tolist()}", flush=True)
+    dc = DevCase(case)
+    if case.new_k is not None:
+        out = dc.step()
+    else:
+        out = dc.decode()
+    torch.cuda.synchronize()
+    ref, _, _ = _reference(case, dc)
+    assert dc.err_bits() == 0
+    assert torch.isfinite(out).all()
+    assert max_abs(out, ref) <= TOL[case.kv_dtype]
