@@ -175,6 +175,30 @@ int nbx_paged_decode_partial(const void *q, int32_t q_dtype, int32_t batch, int3
                              float *l_part, int32_t *dev_err, hipStream_t stream);
 
 /*
+ * nbx_paged_decode_partial_windows - split partials for a batch whose
+ * sequences carry windows of different lengths (several streams' verify
+ * windows in one launch, the ragged case of TensorFold PR #1219's contract).
+ *
+ *   q_rows        the longest window: q is [batch, q_heads, q_rows, head_dim]
+ *                 with each sequence's window in its first rows.
+ *   rows_per_seq  device int32 [batch]: window rows of sequence b, in
+ *                 [0, q_rows] (an entry outside is clamped and sets
+ *                 NBX_DEVERR_SEQ_RANGE).  Causal: row r < rows_per_seq[b] is
+ *                 position seq_lens[b] - rows_per_seq[b] + r and sees keys up to
+ *                 it; rows r >= rows_per_seq[b] are padding, every split of
+ *                 theirs stores m = -inf, l = 0 (their merged output is 0).
+ * Other arguments, layouts and errors as for nbx_paged_decode_partial.
+ */
+int nbx_paged_decode_partial_windows(const void *q, int32_t q_dtype, int32_t batch,
+                                     int32_t q_heads, int32_t q_rows,
+                                     const int32_t *rows_per_seq, int32_t causal,
+                                     const nbx_kv_pool *k_pool, const nbx_kv_pool *v_pool,
+                                     const int32_t *block_table, int32_t max_pages,
+                                     const int32_t *seq_lens, float scale, int32_t split_size,
+                                     int32_t n_split, float *o_part, float *m_part,
+                                     float *l_part, int32_t *dev_err, hipStream_t stream);
+
+/*
  * nbx_paged_decode_merge - fixed-order combine of split partials (nbxtensor
  * attention_wrappers.py, decode_reduce): per row, M = the largest m_s of the
  * non-empty splits (m_s != -inf; the o of an empty split is not read),

@@ -83,6 +83,10 @@ def load_library():
             lib.nbx_paged_decode_step.restype = ctypes.c_int
             lib.nbx_paged_lens_advance.argtypes = [P, I32, I32, P]
             lib.nbx_paged_lens_advance.restype = ctypes.c_int
+            lib.nbx_paged_decode_partial_windows.argtypes = [P, I32, I32, I32, I32, P, I32, PP, PP,
+                                                             P, I32, P, F, I32, I32, P, P, P, P,
+                                                             P]
+            lib.nbx_paged_decode_partial_windows.restype = ctypes.c_int
             lib.nbx_status_str.argtypes = [ctypes.c_int]
             lib.nbx_status_str.restype = ctypes.c_char_p
             lib.nbx_version.restype = ctypes.c_int
@@ -292,3 +296,21 @@ def nbx_paged_lens_advance(seq_lens, n: int, stream=None):
     st = load_library().nbx_paged_lens_advance(_ptr(seq_lens), int(seq_lens.numel()), int(n),
                                                _stream(stream))
     _check(st, "nbx_paged_lens_advance")
+
+
+def nbx_paged_decode_partial_windows(q, k_pool: KVPool, v_pool: KVPool, block_table, seq_lens,
+                                     rows_per_seq, scale: float, split_size: int, n_split: int,
+                                     o_part, m_part, l_part, causal: bool = True, dev_err=None,
+                                     stream=None):
+    """Split partials with a window of rows_per_seq[b] rows for sequence b (q padded
+    to [batch, q_heads, longest window, head_dim])."""
+    kd, vd = _decode_common(q, k_pool, v_pool, block_table, seq_lens)
+    if rows_per_seq.dtype != torch.int32 or rows_per_seq.numel() != q.shape[0]:
+        raise ValueError("rows_per_seq must be int32 [batch]")
+    B, Hq, W, D = q.shape
+    st = load_library().nbx_paged_decode_partial_windows(
+        _ptr(q), _dtype_code(q), B, Hq, W, _ptr(rows_per_seq), int(bool(causal)),
+        ctypes.byref(kd), ctypes.byref(vd), _ptr(block_table), block_table.shape[1],
+        _ptr(seq_lens), float(scale), int(split_size), int(n_split), _ptr(o_part), _ptr(m_part),
+        _ptr(l_part), _ptr(dev_err), _stream(stream))
+    _check(st, "nbx_paged_decode_partial_windows")

@@ -289,6 +289,35 @@ int nbx_paged_decode_partial(const void *q, int32_t q_dtype, int32_t batch, int3
     return to_status(launch_partial(a, stream));
 }
 
+int nbx_paged_decode_partial_windows(const void *q, int32_t q_dtype, int32_t batch,
+                                     int32_t q_heads, int32_t q_rows,
+                                     const int32_t *rows_per_seq, int32_t causal,
+                                     const nbx_kv_pool *k_pool, const nbx_kv_pool *v_pool,
+                                     const int32_t *block_table, int32_t max_pages,
+                                     const int32_t *seq_lens, float scale, int32_t split_size,
+                                     int32_t n_split, float *o_part, float *m_part,
+                                     float *l_part, int32_t *dev_err, hipStream_t stream)
+{
+    if (!rows_per_seq)
+        return NBX_ERR_NULL_PTR;
+    int st = validate_partial(q, q_dtype, batch, q_heads, q_rows, causal, k_pool, v_pool,
+                              block_table, max_pages, seq_lens, scale, split_size, n_split);
+    if (st != NBX_OK)
+        return st;
+    if (!o_part || !m_part || !l_part)
+        return NBX_ERR_NULL_PTR;
+    if (!aligned16(o_part) || ((uintptr_t)m_part & 3u) || ((uintptr_t)l_part & 3u))
+        return NBX_ERR_BAD_ALIGN;
+    if (batch == 0)
+        return NBX_OK;
+    nbx::PartialArgs a =
+        partial_args(q, q_dtype, batch, q_heads, q_rows, causal, k_pool, v_pool, block_table,
+                     max_pages, seq_lens, scale, split_size, n_split, o_part, m_part, l_part,
+                     dev_err);
+    a.rows_per_seq = rows_per_seq;
+    return to_status(launch_partial(a, stream));
+}
+
 int nbx_paged_decode_merge(const float *o_part, const float *m_part, const float *l_part,
                            int64_t rows, int32_t n_split, int32_t head_dim, void *out,
                            int32_t out_dtype, hipStream_t stream)

@@ -46,6 +46,8 @@ struct PartialArgs {
     int32_t split_size, n_split;
     float *o_part, *m_part, *l_part;
     int32_t *dev_err;
+    // ragged windows: rows of sequence b (null: q_rows for every sequence)
+    const int32_t *rows_per_seq;
     // single-launch step (persistent decode kernel): the n_new new positions
     // of each sequence, [batch, n_new, kv_heads, head_dim] of new_dtype, are
     // written by the wave that owns the item holding them
@@ -71,6 +73,34 @@ __device__ inline int device_split_size(const PartialArgs &a)
     const int per = (longest + a.n_split - 1) / a.n_split;
     return (per + 15) / 16 * 16;
 }
+
+// Window rows of sequence b: q_rows, or its rows_per_seq entry clamped to
+// [0, q_rows] (an entry outside sets NBX_DEVERR_SEQ_RANGE when flag_it)
+__device__ inline int seq_window(const PartialArgs &a, int b, bool flag_it)
+{
+    if (!a.rows_per_seq)
+        return a.q_rows;
+    int w = a.rows_per_seq[b];
+    if (w < 0 || w > a.q_rows) {
+        if (flag_it && a.dev_err)
+            atomicOr(a.dev_err, NBX_DEVERR_SEQ_RANGE);
+        w = w < 0 ? 0 : a.q_rows;
+    }
+    return w;
+}
+
+// Keys seen by window row r of a sequence of L keys whose window has wb rows:
+// the window rows are its last wb positions (causal), rows past wb see none
+__device__ inline int row_keys(const PartialArgs &a, int L, int wb, int r)
+{
+    if (r >= wb)
+        return 0;
+    const int n = a.causal ? L - wb + r + 1 : L;
+    return n < 0 ? 0 : n;
+}
+
+// The most keys any window row of the sequence sees
+__device__ inline int seq_keys(int L, int wb) { return wb > 0 ? L : 0; }
 
 struct MergeArgs {
     const float *o_part, *m_part, *l_part;

@@ -257,13 +257,9 @@ decode_mfma_kernel(PartialArgs a)
     if (lead && s == a.n_split - 1 && L > a.n_split * S)
         flag_error(a.dev_err, NBX_DEVERR_SEQ_RANGE);
 
-    int n_j = 0;
-    if (j < M) {
-        n_j = a.causal ? L - a.q_rows + (j % a.q_rows) + 1 : L;
-        n_j = n_j < 0 ? 0 : n_j;
-    }
-    int n_max = a.causal ? L - a.q_rows + min(M, a.q_rows) : L;
-    n_max = n_max < 0 ? 0 : n_max;
+    const int wb = seq_window(a, b, lead && s == 0);
+    const int n_j = j < M ? row_keys(a, L, wb, j % a.q_rows) : 0;
+    const int n_max = seq_keys(L, wb);
     const int j0 = s * S;
     const int jend = min(j0 + S, n_max);
     const int e_j = min(jend, n_j);
@@ -511,7 +507,7 @@ decode_persistent_kernel(PartialArgs a)
 
     // sequence table, lane l of block t describing b = 64 t + l: clamped
     // length, splits holding keys, inclusive prefix of item counts
-    int Lr[NB], nsr[NB], incl[NB];
+    int Lr[NB], Wr[NB], nsr[NB], incl[NB];
     int longest = 1;
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
@@ -526,6 +522,7 @@ decode_persistent_kernel(PartialArgs a)
             }
         }
         Lr[t] = L;
+        Wr[t] = b < a.batch ? seq_window(a, b, wv == 0) : 0;
         longest = max(longest, L);
     }
     // positions per split: the caller's, or (split_size == 0) derived from the
@@ -544,8 +541,7 @@ decode_persistent_kernel(PartialArgs a)
         const int L = Lr[t];
         if (wv == 0 && b < a.batch && (L > NS * S || (FA && L < a.n_new)))
             flag_error(a.dev_err, NBX_DEVERR_SEQ_RANGE);
-        int nmax = a.causal ? L - a.q_rows + min(M, a.q_rows) : L;
-        nmax = nmax < 0 ? 0 : nmax;
+        const int nmax = seq_keys(L, Wr[t]);
         const int ns = b < a.batch ? min((nmax + S - 1) / S, NS) : 0;
         int x = ns * H;
 #pragma unroll
@@ -602,17 +598,11 @@ decode_persistent_kernel(PartialArgs a)
         const int r = k - excl;
         it.s = r / H;
         it.gk = r - it.s * H;
-        const int L = lane_val(Lr, it.b);
-        int nmax = a.causal ? L - a.q_rows + min(M, a.q_rows) : L;
-        nmax = nmax < 0 ? 0 : nmax;
+        const int L = lane_val(Lr, it.b), wb = lane_val(Wr, it.b);
         it.j0 = it.s * S;
-        it.jend = min(it.j0 + S, nmax);
+        it.jend = min(it.j0 + S, seq_keys(L, wb));
         it.nchunk = (it.jend - it.j0 + kChunk - 1) / kChunk;
-        int n_j = 0;
-        if (j < M) {
-            n_j = a.causal ? L - a.q_rows + (j % a.q_rows) + 1 : L;
-            n_j = n_j < 0 ? 0 : n_j;
-        }
+        const int n_j = j < M ? row_keys(a, L, wb, j % a.q_rows) : 0;
         it.e_j = min(it.jend, n_j);
         it.row_base = ((int64_t)it.b * a.q_heads + (int64_t)it.gk * a.group) * a.q_rows;
         it.L = L;
@@ -876,23 +866,16 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
     if (lead && rb == 0 && s == a.n_split - 1 && L > a.n_split * S)
         flag_error(a.dev_err, NBX_DEVERR_SEQ_RANGE);
 
+    const int wb = seq_window(a, b, lead && s == 0 && rb == 0);
     int n_row[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
         const int m = row_lo + (w * NT + n) * 16 + j;
-        int nn = 0;
-        if (m < row_hi) {
-            nn = a.causal ? L - a.q_rows + (m % a.q_rows) + 1 : L;
-            nn = nn < 0 ? 0 : nn;
-        }
-        n_row[n] = nn;
+        n_row[n] = m < row_hi ? row_keys(a, L, wb, m % a.q_rows) : 0;
     }
-    int n_max = L;
-    if (a.causal) {
-        n_max = 0;
-        for (int m = row_lo; m < row_hi && m < row_lo + a.q_rows; ++m)
-            n_max = max(n_max, L - a.q_rows + (m % a.q_rows) + 1);
-    }
+    int n_max = 0;                             // the most keys a row of this block sees
+    for (int m = row_lo; m < row_hi && m < row_lo + a.q_rows; ++m)
+        n_max = max(n_max, row_keys(a, L, wb, m % a.q_rows));
     const int j0 = s * S;
     const int jend = min(j0 + S, n_max);
     const int nchunk = jend > j0 ? (jend - j0 + CH - 1) / CH : 0;

@@ -71,13 +71,9 @@ partial_valu_kernel(PartialArgs a)
         const int i = idx / D, e = idx % D;
         q_s[i][e] = i < rows_here ? load_q<QT>(a.q, (row_base + row0 + i) * D + e) : 0.0f;
     }
+    const int wb = seq_window(a, b, t == 0 && rb == 0 && s == 0);
     if (t < RB) {
-        int n = 0;
-        if (t < rows_here) {
-            const int r = (row0 + t) % a.q_rows;
-            n = a.causal ? L - a.q_rows + r + 1 : L;
-            n = n < 0 ? 0 : n;
-        }
+        const int n = t < rows_here ? row_keys(a, L, wb, (row0 + t) % a.q_rows) : 0;
         n_s[t] = n;
         m_s[t] = -INFINITY;
         l_s[t] = 0.0f;

@@ -20,7 +20,7 @@ def test_every_declared_symbol_is_exported(lib):
     assert {"nbx_paged_kv_append", "nbx_paged_decode_partial", "nbx_paged_decode_merge",
             "nbx_paged_decode", "nbx_paged_decode_plan", "nbx_paged_decode_workspace_bytes",
             "nbx_status_str", "nbx_version", "nbx_paged_decode_step",
-            "nbx_paged_lens_advance"} <= set(names)
+            "nbx_paged_lens_advance", "nbx_paged_decode_partial_windows"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -161,3 +161,15 @@ def test_lens_advance_validation(lib):
     assert lib.nbx_paged_lens_advance(None, 4, 1, None) == -1
     assert lib.nbx_paged_lens_advance(FAKE, -1, 1, None) == -3
     assert lib.nbx_paged_lens_advance(FAKE, 0, 1, None) == 0      # nothing launched
+
+
+def test_windows_validation(lib):
+    k, v = pool(), pool()
+
+    def call(rows=FAKE, q_rows=4, split=256):
+        return lib.nbx_paged_decode_partial_windows(
+            FAKE, 1, 2, 4, q_rows, rows, 1, ctypes.byref(k), ctypes.byref(v), FAKE, 4, FAKE, 0.1,
+            split, 2, FAKE, FAKE, FAKE, None, None)
+    assert call(rows=None) == -1
+    assert call(q_rows=0) == -3
+    assert call(split=24) == -4

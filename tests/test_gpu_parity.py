@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import oracle
+from paged_split_kv_append_amd import binding as nb
 from paged_split_kv_append_amd import synth
 
 from gpu_cases import TOL, DevCase, max_abs
@@ -328,3 +329,69 @@ def test_page_sizes_match_oracle(workload, page_tokens):
     assert dc.err_bits() == 0
     assert torch.isfinite(out).all()
     assert max_abs(out, ref) <= TOL[case.kv_dtype]
+
+
+# ------------------------------------------------------------------ ragged windows
+
+WINDOWS = [
+    # (name, workload, overrides, window rows per sequence)
+    ("verify_d256_bf16", 3, dict(batch=4, lens=("uniform", 300, 900)), [16, 5, 1, 11]),
+    ("decode_gqa_d128", 2, dict(batch=4, q_rows=4, causal=True, lens=("uniform", 8, 700)),
+     [4, 1, 3, 0]),
+    ("chunk_fp8_d256", 4, dict(batch=3, q_rows=32, lens=("uniform", 64, 600)), [32, 7, 20]),
+    ("tiny_f32", 1, dict(batch=3, q_rows=5, causal=True, lens=("uniform", 10, 200),
+                         num_pages=None, max_pages=None), [5, 2, 0]),
+]
+
+
+@pytest.mark.parametrize("name,workload,over,windows", WINDOWS, ids=[w[0] for w in WINDOWS])
+def test_ragged_windows_match_per_sequence_oracle(name, workload, over, windows):
+    """Sequences with windows of different lengths in one launch: each sequence's
+    rows equal the oracle run on that sequence alone with its own window, and
+    padding rows merge to exactly 0."""
+    case = synth.make_case(workload, seed=85, append=False, **over)
+    rows_b = np.array(windows, dtype=np.int32)
+    print(f"windows {name}: {rows_b.tolist()} lens={case.seq_lens.tolist()}", flush=True)
+    dc = DevCase(case)
+    n_split, split = dc.plan()
+    B, Hq, W, D = case.q.shape
+    dev = "cuda"
+    o = torch.empty(case.rows, n_split, D, device=dev)
+    m = torch.empty(case.rows, n_split, device=dev)
+    l = torch.empty(case.rows, n_split, device=dev)
+    kp, vp = dc.pools()
+    nb.nbx_paged_decode_partial_windows(dc.q, kp, vp, dc.bt, dc.lens,
+                                        torch.from_numpy(rows_b).to(dev), case.softmax_scale,
+                                        split, n_split, o, m, l, causal=case.causal,
+                                        dev_err=dc.err)
+    out = torch.empty(case.rows, D, device=dev)
+    nb.nbx_paged_decode_merge(o, m, l, out)
+    torch.cuda.synchronize()
+    assert dc.err_bits() == 0
+    got = out.double().cpu().numpy().reshape(B, Hq, W, D)
+    for b, wb in enumerate(rows_b.tolist()):
+        assert np.all(got[b, :, wb:, :] == 0.0)
+        if wb == 0:
+            continue
+        qb = case.q[b:b + 1, :, :wb, :].contiguous()
+        ref = oracle.attention(qb, case.q_dtype, case.k_pool, case.v_pool, case.kv_dtype,
+                               case.block_table[b:b + 1], case.seq_lens[b:b + 1],
+                               case.softmax_scale, case.causal, case.k_scale, case.v_scale)
+        err = float(np.max(np.abs(got[b, :, :wb, :].reshape(-1, D) - ref)))
+        assert err <= TOL[case.kv_dtype], (b, wb, err)
+
+
+def test_ragged_window_entry_out_of_range_is_flagged():
+    case = synth.make_case(2, seed=86, append=False, batch=2, q_rows=4, causal=True,
+                           lens=("uniform", 8, 300))
+    dc = DevCase(case)
+    n_split, split = dc.plan()
+    o = torch.empty(case.rows, n_split, case.head_dim, device="cuda")
+    m = torch.empty(case.rows, n_split, device="cuda")
+    l = torch.empty_like(m)
+    kp, vp = dc.pools()
+    rows_b = torch.tensor([9, 2], dtype=torch.int32, device="cuda")   # 9 > 4 window rows
+    nb.nbx_paged_decode_partial_windows(dc.q, kp, vp, dc.bt, dc.lens, rows_b, case.softmax_scale,
+                                        split, n_split, o, m, l, causal=True, dev_err=dc.err)
+    torch.cuda.synchronize()
+    assert dc.err_bits() & 0x4

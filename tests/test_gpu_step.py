@@ -313,3 +313,40 @@ def test_step_graph_replays_as_lengths_grow():
         assert dc.err_bits() == 0
         assert torch.isfinite(out).all()
         assert max_abs(out.reshape(case.rows, D), ref) <= TOL["bf16"]
+
+
+def test_prompt_chunk_chain_over_a_growing_cache():
+    """Three 128-row prompt chunks in turn (fp8 pool, the prompt-chunk shape):
+    each step appends its 128 positions and attends causally over the cache so
+    far, through the multi-row path."""
+    chunk, n_chunks = 128, 3
+    case = synth.make_case(4, seed=91, append=False, lens=("fixed", 200 + chunk * n_chunks))
+    final = int(case.seq_lens[0])
+    T, H, D = case.page_tokens, case.kv_heads, case.head_dim
+    first = final - chunk * n_chunks
+    slots = np.array([int(case.block_table[0, p // T]) * T + p % T
+                      for p in range(first, final)], dtype=np.int32)
+    _poison_slots(case, slots)
+    gen = torch.Generator().manual_seed(91)
+    dc = DevCase(case)
+    k_ref, v_ref = case.k_pool, case.v_pool
+    for i in range(n_chunks):
+        L = first + chunk * (i + 1)
+        dc.lens.fill_(L)
+        nk = torch.randn(1, chunk, H, D, generator=gen)
+        nv = torch.randn(1, chunk, H, D, generator=gen)
+        q = torch.randn(1, case.q_heads, chunk, D, generator=gen).to(torch.bfloat16)
+        dc.q.copy_(q)
+        n_split, split = nb.nbx_paged_decode_plan(L, 2048, 16)
+        out = dc.step(nk.cuda(), nv.cuda(), n_split=n_split, split_size=split)
+        torch.cuda.synchronize()
+        sl = slots[chunk * i:chunk * (i + 1)]
+        k_ref, _ = oracle.append(nk.reshape(-1, H, D), "f32", k_ref, "fp8", case.k_scale, T, sl)
+        v_ref, _ = oracle.append(nv.reshape(-1, H, D), "f32", v_ref, "fp8", case.v_scale, T, sl)
+        ref = oracle.attention(q, "bf16", k_ref, v_ref, "fp8", case.block_table,
+                               np.array([L], dtype=np.int32), case.softmax_scale, True,
+                               case.k_scale, case.v_scale)
+        print(f"chunk {i}: keys {L}", flush=True)
+        assert dc.err_bits() == 0
+        assert torch.isfinite(out).all()
+        assert max_abs(out, ref) <= TOL["fp8"]
