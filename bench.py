@@ -37,6 +37,8 @@ WORKLOAD_TEXT = {
        "pool, bf16 Q",
     5: "long mixed decode: B=8, L log-uniform [1024,131072], 64/8 heads, D=128, bf16 T=32, "
        "K x4, append 1 then read",
+    6: "ragged verify windows: 4 sequences with 16, 12, 8 and 4 causal rows, 24/4 heads, D=256, "
+       "32768 keys, bf16 T=16",
 }
 
 
@@ -196,9 +198,10 @@ def log(*a):
 
 def flops_of(case) -> float:
     """QK^T and PV multiply-adds over the keys each row sees (2 flops each)."""
-    W, D = case.q_rows, case.head_dim
+    D = case.head_dim
     tot = 0.0
-    for L in case.seq_lens.astype(np.int64):
+    for b, L in enumerate(case.seq_lens.astype(np.int64)):
+        W = int(case.rows_per_seq[b]) if case.rows_per_seq is not None else case.q_rows
         if case.causal:
             keys = sum(max(0, int(L) - W + r + 1) for r in range(W))
         else:
@@ -213,7 +216,6 @@ def cpu_baseline(case, budget_s: float = 10.0):
     sequences it finished and its share of the append."""
     import oracle
     esz = {"f32": 4, "bf16": 2, "fp8": 1}[case.kv_dtype]
-    rows_per_seq = case.q_heads * case.q_rows
     done_bytes, n_seq, passes, secs = 0, 0, 0, 0.0
     while secs < budget_s:
         t0 = time.perf_counter()
@@ -224,9 +226,12 @@ def cpu_baseline(case, budget_s: float = 10.0):
         t_attn, done = 0.0, 0
         for b in range(case.batch):
             t1 = time.perf_counter()
-            oracle.attention(case.q, case.q_dtype, kp, vp, case.kv_dtype, case.block_table,
-                             case.seq_lens, case.softmax_scale, case.causal, case.k_scale,
-                             case.v_scale, rows=(b * rows_per_seq, (b + 1) * rows_per_seq))
+            wb = int(case.rows_per_seq[b]) if case.rows_per_seq is not None else case.q_rows
+            if wb > 0:                          # the sequence alone, with its own window
+                oracle.attention(case.q[b:b + 1, :, :wb].contiguous(), case.q_dtype, kp, vp,
+                                 case.kv_dtype, case.block_table[b:b + 1],
+                                 case.seq_lens[b:b + 1], case.softmax_scale, case.causal,
+                                 case.k_scale, case.v_scale)
             t_attn += time.perf_counter() - t1
             done_bytes += int(case.seq_lens[b]) * case.kv_heads * case.head_dim * esz * 2
             done += 1
@@ -251,7 +256,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush-mib", type=int, default=1024)
@@ -315,7 +320,10 @@ def main():
     flush = torch.ones(args.flush_mib * (1 << 18), device=dev) if args.flush_mib else None
     stream_ptr = torch.cuda.current_stream().cuda_stream
 
-    fused = not args.unfused
+    windows = case.rows_per_seq is not None
+    if windows:
+        rows_b = torch.from_numpy(case.rows_per_seq).to(dev)
+    fused = not args.unfused and not windows
     if fused:
         ws = torch.empty(nb.nbx_paged_decode_workspace_bytes(rows, n_split, D), dtype=torch.uint8,
                          device=dev)
@@ -342,8 +350,13 @@ def main():
             nb.nbx_paged_kv_append(new_k, new_v, kp, vp, slots, dev_err=err)
         if part_ev is not None:
             part_ev[0].record(stream_ptr)
-        nb.nbx_paged_decode_partial(q, kp, vp, bt, lens, case.softmax_scale, split, n_split,
-                                    o_part, m_part, l_part, causal=case.causal, dev_err=err)
+        if windows:
+            nb.nbx_paged_decode_partial_windows(q, kp, vp, bt, lens, rows_b, case.softmax_scale,
+                                                split, n_split, o_part, m_part, l_part,
+                                                causal=case.causal, dev_err=err)
+        else:
+            nb.nbx_paged_decode_partial(q, kp, vp, bt, lens, case.softmax_scale, split, n_split,
+                                        o_part, m_part, l_part, causal=case.causal, dev_err=err)
         if part_ev is not None:
             part_ev[1].record(stream_ptr)
         nb.nbx_paged_decode_merge(o_part, m_part, l_part, out)
@@ -433,6 +446,8 @@ def main():
                              "launch, then the merge" if has_append else
                              "nbx_paged_decode_step: split partials, then the merge")
                             if fused else
+                            "nbx_paged_decode_partial_windows, nbx_paged_decode_merge"
+                            if windows else
                             "nbx_paged_kv_append, nbx_paged_decode_partial, "
                             "nbx_paged_decode_merge"),
                    "n_split": n_split, "split_size": split, "rows": rows,

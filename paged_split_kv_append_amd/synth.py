@@ -19,6 +19,8 @@ Workloads follow the five shapes this library is measured on:
 5. ``long``      batch 8, lengths log-uniform in [1024, 131072], 64 / 8 heads,
                  D=128, bf16 pool with 32-position fragmented pages, K stored x4
                  (peaked logits), one new token appended per sequence first.
+6. ``windows``   the verify shape with windows of 16, 12, 8 and 4 rows for its
+                 four sequences (Q padded to 16 rows).
 
 Random streams: ``numpy.random.SeedSequence(seed).spawn(8)`` in the fixed roles
 [lengths, page order, q, k, v, new k, new v, spare]; the default seed of a
@@ -55,6 +57,10 @@ WORKLOADS = {
             q_dtype=BF16, page_tokens=32, q_rows=1, causal=False,
             lens=("loguniform", 1024, 131072), split=("rule", 256, 64), append=True,
             k_mult=4.0),
+    6: dict(name="windows", batch=4, q_heads=24, kv_heads=4, head_dim=256, kv_dtype=BF16,
+            q_dtype=BF16, page_tokens=16, q_rows=16, causal=True,
+            lens=("fixed", 32768), split=("rule", 256, 64), append=False, k_mult=1.0,
+            windows=(16, 12, 8, 4)),
 }
 
 _TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16}
@@ -88,6 +94,7 @@ class PagedCase:
     new_k: Optional[torch.Tensor] = None     # [N_tok, H_kv, D] fp32
     new_v: Optional[torch.Tensor] = None
     slot_mapping: Optional[np.ndarray] = None  # [N_tok] int32
+    rows_per_seq: Optional[np.ndarray] = None  # [B] int32 window rows (ragged windows)
 
     @property
     def rows(self) -> int:
@@ -216,7 +223,8 @@ def make_case(workload: int, seed: Optional[int] = None, poison: bool = True,
         seq_lens=lens.astype(np.int32), block_table=bt, q=q,
         k_pool=k_pool, v_pool=v_pool, k_scale=k_scale, v_scale=v_scale,
         softmax_scale=float(np.float32(1.0 / math.sqrt(D))),
-        split_policy=split_policy, new_k=new_k, new_v=new_v, slot_mapping=slots)
+        split_policy=split_policy, new_k=new_k, new_v=new_v, slot_mapping=slots,
+        rows_per_seq=(np.array(cfg["windows"], dtype=np.int32) if cfg.get("windows") else None))
 
 
 def describe(workload: int) -> str:

@@ -395,3 +395,36 @@ def test_ragged_window_entry_out_of_range_is_flagged():
                                         split, n_split, o, m, l, causal=True, dev_err=dc.err)
     torch.cuda.synchronize()
     assert dc.err_bits() & 0x4
+
+
+def test_ragged_windows_full_size_sampled():
+    """The four-stream ragged-window shape at full size (32768 keys): the
+    4-row stream in full and the first 48 rows of the 16-row stream."""
+    case = synth.make_case(6)
+    print(f"full-size windows {case.rows_per_seq.tolist()} kv_bytes={case.kv_bytes()}", flush=True)
+    dc = DevCase(case)
+    n_split, split = dc.plan()
+    B, Hq, W, D = case.q.shape
+    o = torch.empty(case.rows, n_split, D, device="cuda")
+    m = torch.empty(case.rows, n_split, device="cuda")
+    l = torch.empty_like(m)
+    kp, vp = dc.pools()
+    nb.nbx_paged_decode_partial_windows(dc.q, kp, vp, dc.bt, dc.lens,
+                                        torch.from_numpy(case.rows_per_seq).cuda(),
+                                        case.softmax_scale, split, n_split, o, m, l, causal=True,
+                                        dev_err=dc.err)
+    out = torch.empty(case.rows, D, device="cuda")
+    nb.nbx_paged_decode_merge(o, m, l, out)
+    torch.cuda.synchronize()
+    assert dc.err_bits() == 0
+    got = out.double().cpu().numpy().reshape(B, Hq, W, D)
+    for b, rows in ((3, None), (0, (0, 48))):
+        wb = int(case.rows_per_seq[b])
+        assert np.all(got[b, :, wb:, :] == 0.0)
+        ref = oracle.attention(case.q[b:b + 1, :, :wb].contiguous(), case.q_dtype, case.k_pool,
+                               case.v_pool, case.kv_dtype, case.block_table[b:b + 1],
+                               case.seq_lens[b:b + 1], case.softmax_scale, True, rows=rows)
+        g = got[b, :, :wb, :].reshape(-1, D)
+        r0, r1 = rows if rows else (0, g.shape[0])
+        err = float(np.max(np.abs(g[r0:r1] - ref[r0:r1])))
+        assert err <= TOL["bf16"], (b, err)
