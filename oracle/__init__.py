@@ -26,7 +26,7 @@ _lib = None
 
 MUTATIONS = {
     "none": 0, "drop_last_split": 1, "head_mod": 2, "causal_off_by_one": 3,
-    "swap_kv": 4, "shift_sign": 5, "page_offset": 6,
+    "swap_kv": 4, "shift_sign": 5, "page_offset": 6, "value_width": 7,
 }
 
 
@@ -53,7 +53,7 @@ def _load():
             lib.oracle_append.argtypes = [P, I, I64, I, I, P, I, D, I64, I, P]
             lib.oracle_append.restype = I
             lib.oracle_split_plan.argtypes = [I64, I64, I64, I64, P, P]
-            common = [P, I, I, I, I, I, I, P, P, I, D, D, I64, I, I, P, I, P, D]
+            common = [P, I, I, I, I, I, I, I, P, P, I, D, D, I64, I, I, P, I, P, D]
             lib.oracle_attention_rows.argtypes = common + [I64, I64, P]
             lib.oracle_attention_rows.restype = I
             lib.oracle_attention.argtypes = common + [P]
@@ -150,26 +150,28 @@ def _problem_args(q, q_dtype, k_pool, v_pool, kv_dtype, k_scale, v_scale, block_
     B, Hq, W, D = qn.shape
     assert W == q_rows
     P, Hkv, T, Dk = kn.shape
-    assert Dk == D and vn.shape == kn.shape
+    Dv = vn.shape[3]
+    assert Dk == D and vn.shape[:3] == kn.shape[:3]
     bt = np.ascontiguousarray(np.asarray(block_table, dtype=np.int32))
     sl = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
     keep = (qn, kn, vn, bt, sl)
-    args = [_ptr(qn), _CODES[q_dtype], B, Hq, W, D, int(bool(causal)), _ptr(kn), _ptr(vn),
+    args = [_ptr(qn), _CODES[q_dtype], B, Hq, W, D, Dv, int(bool(causal)), _ptr(kn), _ptr(vn),
             _CODES[kv_dtype], float(k_scale), float(v_scale), P, Hkv, T, _ptr(bt),
             bt.shape[1], _ptr(sl), float(scale)]
-    return args, keep, (B, Hq, W, D)
+    return args, keep, (B, Hq, W, Dv)
 
 
 def attention(q, q_dtype, k_pool, v_pool, kv_dtype, block_table, seq_lens, scale,
               causal=False, k_scale=1.0, v_scale=1.0, rows=None) -> np.ndarray:
-    """Plain-definition attention in float64: out [B*H_q*W, D] (rows (b, h, r)).
+    """Plain-definition attention in float64: out [B*H_q*W, Dv] (rows (b, h, r)), Dv
+    the value pool's head dim (which may differ from that of q and k).
 
     ``rows``: optional (begin, end) to compute only a sample of rows (others NaN)."""
     W = _np(q).shape[2]
-    args, keep, (B, Hq, W, D) = _problem_args(q, q_dtype, k_pool, v_pool, kv_dtype, k_scale,
-                                              v_scale, block_table, seq_lens, scale, causal, W)
+    args, keep, (B, Hq, W, Dv) = _problem_args(q, q_dtype, k_pool, v_pool, kv_dtype, k_scale,
+                                               v_scale, block_table, seq_lens, scale, causal, W)
     nrows = B * Hq * W
-    out = np.full((nrows, D), np.nan)
+    out = np.full((nrows, Dv), np.nan)
     r0, r1 = (0, nrows) if rows is None else rows
     st = _load().oracle_attention_rows(*args, r0, r1, _ptr(out))
     if st != 0:
@@ -179,12 +181,12 @@ def attention(q, q_dtype, k_pool, v_pool, kv_dtype, block_table, seq_lens, scale
 
 def partials(q, q_dtype, k_pool, v_pool, kv_dtype, block_table, seq_lens, scale, split_len,
              n_split, causal=False, k_scale=1.0, v_scale=1.0):
-    """Per-split (o, m, l) in float64: o [rows, n_split, D], m, l [rows, n_split]."""
+    """Per-split (o, m, l) in float64: o [rows, n_split, Dv], m, l [rows, n_split]."""
     W = _np(q).shape[2]
-    args, keep, (B, Hq, W, D) = _problem_args(q, q_dtype, k_pool, v_pool, kv_dtype, k_scale,
-                                              v_scale, block_table, seq_lens, scale, causal, W)
+    args, keep, (B, Hq, W, Dv) = _problem_args(q, q_dtype, k_pool, v_pool, kv_dtype, k_scale,
+                                               v_scale, block_table, seq_lens, scale, causal, W)
     nrows = B * Hq * W
-    o = np.zeros((nrows, n_split, D))
+    o = np.zeros((nrows, n_split, Dv))
     m = np.zeros((nrows, n_split))
     l = np.zeros((nrows, n_split))
     st = _load().oracle_partials(*args, int(split_len), int(n_split), _ptr(o), _ptr(m), _ptr(l))

@@ -27,7 +27,10 @@
  *    _math_attention: scores, softmax, then P V), gathered through the block
  *    table (nbxtensor paged_decode_attn.py, module description).  GQA head map
  *    h_kv = h div G (paged_decode_attn_split_kernel).  A row that sees no key
- *    is 0 (attention_wrappers.py, the fully-masked-row guard).
+ *    is 0 (attention_wrappers.py, the fully-masked-row guard).  The value
+ *    head dimension Dv is its own size, independent of the D of q and k
+ *    (_math_attention's value head_dim; the split kernel's D_V), so outputs
+ *    and partial outputs have Dv columns.
  *  - oracle_partials: per split s over [s*S, min((s+1)*S, n)), the running max
  *    m, the sum of exp(s_j - m) and the unnormalised sum of exp(s_j - m) v_j
  *    (paged_decode_attn_split_kernel, the stored opart / mpart / lpart).  An
@@ -60,6 +63,7 @@ enum {
     ORC_MUT_SWAP_KV = 4,           /* K and V pools exchanged */
     ORC_MUT_NO_MAX_SHIFT_SIGN = 5, /* exp(m - s) instead of exp(s - m) */
     ORC_MUT_PAGE_OFFSET = 6,       /* position in page taken as j mod T + 1 (wraps) */
+    ORC_MUT_V_WIDTH = 7,           /* V rows addressed with the q/k head dim D, not Dv */
 };
 static int g_mutation = ORC_MUT_NONE;
 
@@ -240,7 +244,7 @@ void oracle_split_plan(int64_t longest, int64_t positions, int64_t max_splits, i
 
 typedef struct {
     const void *q; int q_dtype;
-    int B, Hq, W, D, causal;
+    int B, Hq, W, D, Dv, causal;
     const void *kpool, *vpool; int kv_dtype; double k_scale, v_scale;
     int64_t P; int Hkv, T;
     const int32_t *block_table; int max_pages;
@@ -269,9 +273,10 @@ static int kv_head_of(const orc_problem *pr, int h)
     return h / G;
 }
 
-/* element offset of (logical position j, KV head g, element e) of sequence b,
- * or -1 if the block table does not map position j to a page of the pool */
-static int64_t gather_offset(const orc_problem *pr, int b, int g, int64_t j, int e)
+/* element offset of (logical position j, KV head g, element e) of sequence b
+ * in a pool whose rows hold `width` elements, or -1 if the block table does
+ * not map position j to a page of the pool */
+static int64_t gather_offset(const orc_problem *pr, int b, int g, int64_t j, int e, int width)
 {
     int64_t page = pr->block_table[(int64_t)b * pr->max_pages + j / pr->T];
     int64_t pos = j % pr->T;
@@ -279,7 +284,7 @@ static int64_t gather_offset(const orc_problem *pr, int b, int g, int64_t j, int
         pos = (pos + 1) % pr->T;
     if (page < 0 || page >= pr->P)
         return -1;
-    return ((page * pr->Hkv + g) * pr->T + pos) * pr->D + e;
+    return ((page * pr->Hkv + g) * pr->T + pos) * width + e;
 }
 
 static const void *k_src(const orc_problem *pr)
@@ -301,7 +306,7 @@ static int row_scores(const orc_problem *pr, int b, int h, int r, int64_t j0, in
     double ks = g_mutation == ORC_MUT_SWAP_KV ? pr->v_scale : pr->k_scale;
     for (int64_t j = j0; j < j1; ++j) {
         double acc = 0.0;
-        int64_t base = gather_offset(pr, b, g, j, 0);
+        int64_t base = gather_offset(pr, b, g, j, 0, pr->D);
         if (base < 0)
             return -1;
         for (int e = 0; e < pr->D; ++e)
@@ -332,33 +337,34 @@ static double weight(double s, double m)
     return exp(s - m);
 }
 
-/* sum_j w_j v_j into o[D]; returns -1 on a bad page */
+/* sum_j w_j v_j into o[Dv]; returns -1 on a bad page */
 static int weighted_values(const orc_problem *pr, int b, int h, int64_t j0, int64_t j1,
                            const double *w, double *o)
 {
     int g = kv_head_of(pr, h);
     const void *vp = v_src(pr);
     double vs = g_mutation == ORC_MUT_SWAP_KV ? pr->k_scale : pr->v_scale;
-    for (int e = 0; e < pr->D; ++e)
+    int width = g_mutation == ORC_MUT_V_WIDTH ? pr->D : pr->Dv;
+    for (int e = 0; e < pr->Dv; ++e)
         o[e] = 0.0;
     for (int64_t j = j0; j < j1; ++j) {
-        int64_t base = gather_offset(pr, b, g, j, 0);
+        int64_t base = gather_offset(pr, b, g, j, 0, width);
         if (base < 0)
             return -1;
-        for (int e = 0; e < pr->D; ++e)
+        for (int e = 0; e < pr->Dv; ++e)
             o[e] += w[j - j0] * (oracle_decode_value(pr->kv_dtype, vp, base + e) * vs);
     }
     return 0;
 }
 
 static orc_problem make_problem(const void *q, int q_dtype, int B, int Hq, int W, int D,
-                                int causal, const void *kpool, const void *vpool,
+                                int Dv, int causal, const void *kpool, const void *vpool,
                                 int kv_dtype, double k_scale, double v_scale, int64_t P,
                                 int Hkv, int T, const int32_t *block_table, int max_pages,
                                 const int32_t *seq_lens, double scale)
 {
     orc_problem pr;
-    pr.q = q; pr.q_dtype = q_dtype; pr.B = B; pr.Hq = Hq; pr.W = W; pr.D = D;
+    pr.q = q; pr.q_dtype = q_dtype; pr.B = B; pr.Hq = Hq; pr.W = W; pr.D = D; pr.Dv = Dv;
     pr.causal = causal; pr.kpool = kpool; pr.vpool = vpool; pr.kv_dtype = kv_dtype;
     pr.k_scale = k_scale; pr.v_scale = v_scale; pr.P = P; pr.Hkv = Hkv; pr.T = T;
     pr.block_table = block_table; pr.max_pages = max_pages; pr.seq_lens = seq_lens;
@@ -366,31 +372,34 @@ static orc_problem make_problem(const void *q, int q_dtype, int B, int Hq, int W
     return pr;
 }
 
-/* out: [B*Hq*W, D] doubles, rows ordered (b, h, r).  Only rows
+/* out: [B*Hq*W, Dv] doubles, rows ordered (b, h, r).  Only rows
  * [row_begin, row_end) are computed (a bounded sample); others untouched.
  * Returns 0, or -1 if some visible position has no page in the pool. */
-int oracle_attention_rows(const void *q, int q_dtype, int B, int Hq, int W, int D, int causal,
+int oracle_attention_rows(const void *q, int q_dtype, int B, int Hq, int W, int D, int Dv,
+                          int causal,
                           const void *kpool, const void *vpool, int kv_dtype,
                           double k_scale, double v_scale, int64_t P, int Hkv, int T,
                           const int32_t *block_table, int max_pages, const int32_t *seq_lens,
                           double scale, int64_t row_begin, int64_t row_end, double *out)
 {
-    orc_problem pr = make_problem(q, q_dtype, B, Hq, W, D, causal, kpool, vpool, kv_dtype,
+    orc_problem pr = make_problem(q, q_dtype, B, Hq, W, D, Dv, causal, kpool, vpool, kv_dtype,
                                   k_scale, v_scale, P, Hkv, T, block_table, max_pages,
                                   seq_lens, scale);
     int status = 0;
     if (Hkv <= 0 || Hq % Hkv != 0)
         return -2;
+    if ((g_mutation == ORC_MUT_SWAP_KV && D != Dv) || (g_mutation == ORC_MUT_V_WIDTH && D > Dv))
+        return -2;                                /* would read past a pool */
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t row = row_begin; row < row_end; ++row) {
         int r = (int)(row % W);
         int h = (int)((row / W) % Hq);
         int b = (int)(row / ((int64_t)W * Hq));
         int64_t n = visible_keys(&pr, b, r);
-        double *o = out + row * D;
+        double *o = out + row * Dv;
         double *s, m, den = 0.0;
         if (n == 0) {
-            for (int e = 0; e < D; ++e)
+            for (int e = 0; e < Dv; ++e)
                 o[e] = 0.0;
             continue;
         }
@@ -410,37 +419,41 @@ int oracle_attention_rows(const void *q, int q_dtype, int B, int Hq, int W, int 
 #pragma omp atomic write
             status = -1;
         }
-        for (int e = 0; e < D; ++e)
+        for (int e = 0; e < Dv; ++e)
             o[e] /= den;
         free(s);
     }
     return status;
 }
 
-int oracle_attention(const void *q, int q_dtype, int B, int Hq, int W, int D, int causal,
+int oracle_attention(const void *q, int q_dtype, int B, int Hq, int W, int D, int Dv,
+                     int causal,
                      const void *kpool, const void *vpool, int kv_dtype, double k_scale,
                      double v_scale, int64_t P, int Hkv, int T, const int32_t *block_table,
                      int max_pages, const int32_t *seq_lens, double scale, double *out)
 {
-    return oracle_attention_rows(q, q_dtype, B, Hq, W, D, causal, kpool, vpool, kv_dtype,
+    return oracle_attention_rows(q, q_dtype, B, Hq, W, D, Dv, causal, kpool, vpool, kv_dtype,
                                  k_scale, v_scale, P, Hkv, T, block_table, max_pages, seq_lens,
                                  scale, 0, (int64_t)B * Hq * W, out);
 }
 
-/* o: [rows, n_split, D], m, l: [rows, n_split]. */
-int oracle_partials(const void *q, int q_dtype, int B, int Hq, int W, int D, int causal,
+/* o: [rows, n_split, Dv], m, l: [rows, n_split]. */
+int oracle_partials(const void *q, int q_dtype, int B, int Hq, int W, int D, int Dv,
+                    int causal,
                     const void *kpool, const void *vpool, int kv_dtype, double k_scale,
                     double v_scale, int64_t P, int Hkv, int T, const int32_t *block_table,
                     int max_pages, const int32_t *seq_lens, double scale,
                     int64_t split_len, int n_split, double *o, double *m, double *l)
 {
-    orc_problem pr = make_problem(q, q_dtype, B, Hq, W, D, causal, kpool, vpool, kv_dtype,
+    orc_problem pr = make_problem(q, q_dtype, B, Hq, W, D, Dv, causal, kpool, vpool, kv_dtype,
                                   k_scale, v_scale, P, Hkv, T, block_table, max_pages,
                                   seq_lens, scale);
     int64_t rows = (int64_t)B * Hq * W;
     int status = 0;
     if (Hkv <= 0 || Hq % Hkv != 0)
         return -2;
+    if ((g_mutation == ORC_MUT_SWAP_KV && D != Dv) || (g_mutation == ORC_MUT_V_WIDTH && D > Dv))
+        return -2;                                /* would read past a pool */
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t row = 0; row < rows; ++row) {
         int r = (int)(row % W);
@@ -450,12 +463,12 @@ int oracle_partials(const void *q, int q_dtype, int B, int Hq, int W, int D, int
         double *s = (double *)malloc(sizeof(double) * (size_t)(split_len > 0 ? split_len : 1));
         for (int sp = 0; sp < n_split; ++sp) {
             int64_t j0 = (int64_t)sp * split_len, j1 = j0 + split_len;
-            double *os = o + (row * n_split + sp) * D;
+            double *os = o + (row * n_split + sp) * Dv;
             double mm, ll = 0.0;
             if (j1 > n)
                 j1 = n;
             if (j0 >= j1) {                       /* empty split */
-                for (int e = 0; e < D; ++e)
+                for (int e = 0; e < Dv; ++e)
                     os[e] = 0.0;
                 m[row * n_split + sp] = -INFINITY;
                 l[row * n_split + sp] = 0.0;

@@ -21,6 +21,10 @@ Workloads follow the five shapes this library is measured on:
                  (peaked logits), one new token appended per sequence first.
 6. ``windows``   the verify shape with windows of 16, 12, 8 and 4 rows for its
                  four sequences (Q padded to 16 rows).
+7. ``mla``       the batched decode shape with latent-attention head sizes: q and
+                 k rows of 192, v rows of 128 (value head dim independent of the
+                 query/key one), 16 query heads each with its own KV head,
+                 lengths uniform in [1, 4096], bf16, one new token appended.
 
 Random streams: ``numpy.random.SeedSequence(seed).spawn(8)`` in the fixed roles
 [lengths, page order, q, k, v, new k, new v, spare]; the default seed of a
@@ -61,6 +65,9 @@ WORKLOADS = {
             q_dtype=BF16, page_tokens=16, q_rows=16, causal=True,
             lens=("fixed", 32768), split=("rule", 256, 64), append=False, k_mult=1.0,
             windows=(16, 12, 8, 4)),
+    7: dict(name="mla", batch=32, q_heads=16, kv_heads=16, head_dim=192, v_head_dim=128,
+            kv_dtype=BF16, q_dtype=BF16, page_tokens=16, q_rows=1, causal=False,
+            lens=("uniform", 1, 4096), split=("rule", 256, 64), append=True, k_mult=1.0),
 }
 
 _TORCH_DTYPE = {F32: torch.float32, BF16: torch.bfloat16}
@@ -86,15 +93,20 @@ class PagedCase:
     block_table: np.ndarray         # [B, max_pages] int32, -1 padded
     q: torch.Tensor                 # [B, H_q, W, D] fp32 or bf16
     k_pool: torch.Tensor            # [P, H_kv, T, D] fp32 / bf16 / uint8 (e4m3 codes)
-    v_pool: torch.Tensor
+    v_pool: torch.Tensor            # [P, H_kv, T, Dv]
     k_scale: float                  # fp32 dequant factor (1.0 unless fp8)
     v_scale: float
     softmax_scale: float            # an fp32 value: 1/sqrt(D) rounded to fp32
     split_policy: tuple             # ("fixed", S, n) or ("rule", positions, cap)
     new_k: Optional[torch.Tensor] = None     # [N_tok, H_kv, D] fp32
-    new_v: Optional[torch.Tensor] = None
+    new_v: Optional[torch.Tensor] = None     # [N_tok, H_kv, Dv] fp32
     slot_mapping: Optional[np.ndarray] = None  # [N_tok] int32
     rows_per_seq: Optional[np.ndarray] = None  # [B] int32 window rows (ragged windows)
+    v_head_dim: int = 0                     # Dv, the V pool's head dim (0: = head_dim)
+
+    def __post_init__(self):
+        if not self.v_head_dim:
+            self.v_head_dim = self.head_dim
 
     @property
     def rows(self) -> int:
@@ -103,7 +115,8 @@ class PagedCase:
     def kv_bytes(self) -> int:
         """Algorithmic K/V bytes one read pass touches (each element once)."""
         esz = {F32: 4, BF16: 2, FP8: 1}[self.kv_dtype]
-        return int(self.seq_lens.astype(np.int64).sum()) * self.kv_heads * self.head_dim * esz * 2
+        return (int(self.seq_lens.astype(np.int64).sum()) * self.kv_heads *
+                (self.head_dim + self.v_head_dim) * esz)
 
 
 def _draw_lens(spec, batch, rng):
@@ -163,6 +176,7 @@ def make_case(workload: int, seed: Optional[int] = None, poison: bool = True,
     r_len, r_page, r_q, r_k, r_v, r_nk, r_nv, _ = [np.random.default_rng(s) for s in ss]
 
     B, Hq, Hkv, D = cfg["batch"], cfg["q_heads"], cfg["kv_heads"], cfg["head_dim"]
+    Dv = int(cfg.get("v_head_dim") or D)
     T, W = cfg["page_tokens"], cfg["q_rows"]
     lens = _draw_lens(cfg["lens"], B, r_len)
     lens = np.maximum(lens, W if cfg["causal"] else 1)
@@ -179,15 +193,14 @@ def make_case(workload: int, seed: Optional[int] = None, poison: bool = True,
         bt[b, :n] = order[off:off + n]
         off += n
 
-    nkv = P * Hkv * T * D
-    kf = _normals(r_k, nkv, cfg["k_mult"]).view(P, Hkv, T, D)
-    vf = _normals(r_v, nkv).view(P, Hkv, T, D)
+    kf = _normals(r_k, P * Hkv * T * D, cfg["k_mult"]).view(P, Hkv, T, D)
+    vf = _normals(r_v, P * Hkv * T * Dv).view(P, Hkv, T, Dv)
     q = _normals(r_q, B * Hq * W * D).view(B, Hq, W, D).to(_TORCH_DTYPE[cfg["q_dtype"]])
 
     new_k = new_v = slots = None
     if cfg["append"]:
         new_k = _normals(r_nk, B * Hkv * D, cfg["k_mult"]).view(B, Hkv, D)
-        new_v = _normals(r_nv, B * Hkv * D).view(B, Hkv, D)
+        new_v = _normals(r_nv, B * Hkv * Dv).view(B, Hkv, Dv)
         pos = lens - 1
         slots = (bt[np.arange(B), pos // T].astype(np.int64) * T + pos % T).astype(np.int32)
 
@@ -224,11 +237,13 @@ def make_case(workload: int, seed: Optional[int] = None, poison: bool = True,
         k_pool=k_pool, v_pool=v_pool, k_scale=k_scale, v_scale=v_scale,
         softmax_scale=float(np.float32(1.0 / math.sqrt(D))),
         split_policy=split_policy, new_k=new_k, new_v=new_v, slot_mapping=slots,
-        rows_per_seq=(np.array(cfg["windows"], dtype=np.int32) if cfg.get("windows") else None))
+        rows_per_seq=(np.array(cfg["windows"], dtype=np.int32) if cfg.get("windows") else None),
+        v_head_dim=Dv)
 
 
 def describe(workload: int) -> str:
     c = WORKLOADS[workload]
-    return (f"{c['name']}: B={c['batch']} Hq={c['q_heads']} Hkv={c['kv_heads']} D={c['head_dim']} "
+    dv = f"/{c['v_head_dim']}" if c.get("v_head_dim") else ""
+    return (f"{c['name']}: B={c['batch']} Hq={c['q_heads']} Hkv={c['kv_heads']} D={c['head_dim']}{dv} "
             f"W={c['q_rows']} causal={c['causal']} kv={c['kv_dtype']} T={c['page_tokens']} "
             f"lens={c['lens']}")

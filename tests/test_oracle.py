@@ -5,7 +5,8 @@ library routines on special cases (torch's fp8 / bf16 casts, torch's float64
 scaled-dot-product attention), closed forms of softmax attention, a worked
 example printed on the maxdiffusion PR #477 page, hand-written append and split
 examples, and invariants (page placement, GQA = replicated MHA, zero-padded
-head dim, the merge identity, causal rows = shorter decodes).  The last tests
+head dim, the merge identity, causal rows = shorter decodes, value columns
+computed independently of the value head dim).  The last tests
 plant known mistakes in the oracle and require that some pin goes red.
 """
 import json
@@ -25,18 +26,20 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 # ----------------------------------------------------------------- helpers
 
 def contiguous_problem(seed, B=2, Hq=4, Hkv=2, W=1, D=16, T=16, lens=(37, 50), causal=False,
-                       kv_dtype="f32"):
-    """Random contiguous K/V [B, Hkv, L, D] laid into pages through an identity table."""
+                       kv_dtype="f32", Dv=None):
+    """Random contiguous K [B, Hkv, L, D] and V [B, Hkv, L, Dv] laid into pages through an
+    identity table (Dv defaults to D)."""
+    Dv = D if Dv is None else Dv
     g = torch.Generator().manual_seed(seed)
     L = max(lens)
     pages = -(-L // T)
     Kc = torch.randn(B, Hkv, pages * T, D, generator=g, dtype=torch.float64)
-    Vc = torch.randn(B, Hkv, pages * T, D, generator=g, dtype=torch.float64)
+    Vc = torch.randn(B, Hkv, pages * T, Dv, generator=g, dtype=torch.float64)
     Q = torch.randn(B, Hq, W, D, generator=g, dtype=torch.float64)
     if kv_dtype == "f32":
         Kc, Vc, Q = Kc.float().double(), Vc.float().double(), Q.float().double()
     pool_k = Kc.view(B, Hkv, pages, T, D).permute(0, 2, 1, 3, 4).reshape(B * pages, Hkv, T, D)
-    pool_v = Vc.view(B, Hkv, pages, T, D).permute(0, 2, 1, 3, 4).reshape(B * pages, Hkv, T, D)
+    pool_v = Vc.view(B, Hkv, pages, T, Dv).permute(0, 2, 1, 3, 4).reshape(B * pages, Hkv, T, Dv)
     bt = np.arange(B * pages, dtype=np.int32).reshape(B, pages)
     return dict(Q=Q, K=Kc, V=Vc, pool_k=pool_k.float(), pool_v=pool_v.float(), bt=bt,
                 lens=np.array(lens, dtype=np.int32), causal=causal, W=W)
@@ -50,7 +53,8 @@ def oracle_on(p, scale, **kw):
 def sdpa_reference(p, scale):
     """torch's float64 scaled_dot_product_attention per sequence (library routine)."""
     Q, K, V, lens = p["Q"], p["K"], p["V"], p["lens"]
-    B, Hq, W, D = Q.shape
+    B, Hq, W, _ = Q.shape
+    Dv = V.shape[-1]
     G = Hq // K.shape[1]
     outs = []
     for b in range(B):
@@ -64,7 +68,7 @@ def sdpa_reference(p, scale):
             mask = j <= (L - W + r)
         o = torch.nn.functional.scaled_dot_product_attention(Q[b], k, v, attn_mask=mask,
                                                              scale=scale)
-        outs.append(o.reshape(Hq * W, D))
+        outs.append(o.reshape(Hq * W, Dv))
     return torch.cat(outs).numpy()
 
 
@@ -269,6 +273,23 @@ def test_matches_torch_sdpa_float64(seed, W, causal, Hq, Hkv, D, T, lens):
     assert np.allclose(oracle_on(p, scale), sdpa_reference(p, scale), atol=1e-12, rtol=0)
 
 
+# value head dim independent of the query/key one (nbxtensor attention_wrappers.py,
+# _math_attention; the split kernel's D_V): torch's attention takes a value width of
+# its own too
+@pytest.mark.parametrize("seed,W,causal,Hq,Hkv,D,Dv,lens", [
+    (14, 1, False, 4, 4, 24, 16, (37, 50)),
+    (15, 3, True, 6, 2, 16, 40, (20, 61)),
+    (16, 1, False, 8, 2, 48, 32, (1, 95)),
+])
+def test_value_head_dim_matches_torch_sdpa_float64(seed, W, causal, Hq, Hkv, D, Dv, lens):
+    p = contiguous_problem(seed, B=len(lens), Hq=Hq, Hkv=Hkv, W=W, D=D, Dv=Dv, lens=lens,
+                           causal=causal)
+    scale = float(np.float32(1 / math.sqrt(D)))
+    out = oracle_on(p, scale)
+    assert out.shape == (len(lens) * Hq * W, Dv)
+    assert np.allclose(out, sdpa_reference(p, scale), atol=1e-12, rtol=0)
+
+
 # ----------------------------------------------------------------- invariants
 
 def test_page_placement_invariance_is_exact():
@@ -303,6 +324,38 @@ def test_zero_padding_the_head_dim_is_exact():
     p2 = dict(p, Q=pad(p["Q"]), pool_k=pad(p["pool_k"]), pool_v=pad(p["pool_v"]))
     padded = oracle_on(p2, 0.25)          # scale stays at the true D
     assert np.allclose(padded[:, :16], base, atol=1e-14) and np.all(padded[:, 16:] == 0)
+
+
+def test_value_columns_do_not_depend_on_the_value_width():
+    # each output column is the same weighted sum whatever other columns V has:
+    # V of 48 columns, then its first 16 and its last 32 as pools of their own
+    p = contiguous_problem(25, Hq=6, Hkv=3, W=2, D=32, Dv=48, lens=(29, 47), causal=True)
+    wide = oracle_on(p, 0.2)
+    lo = oracle_on(dict(p, pool_v=p["pool_v"][..., :16].contiguous()), 0.2)
+    hi = oracle_on(dict(p, pool_v=p["pool_v"][..., 16:].contiguous()), 0.2)
+    assert np.all(np.isfinite(wide))
+    assert np.array_equal(wide[:, :16], lo) and np.array_equal(wide[:, 16:], hi)
+
+
+def test_uniform_logits_with_a_narrower_value_head():
+    p = contiguous_problem(26, Hq=4, Hkv=2, D=40, Dv=8, lens=(13, 30))
+    p["Q"] = torch.zeros_like(p["Q"])
+    out = oracle_on(p, 0.5)
+    for b in range(2):
+        for h in range(4):
+            ref = p["V"][b, h // 2, :int(p["lens"][b])].mean(0).numpy()
+            assert np.allclose(out[b * 4 + h], ref, atol=1e-12)
+
+
+def test_merge_identity_with_a_value_head_of_its_own():
+    c = synth.make_case(7, seed=27, batch=3, lens=("uniform", 1, 200), append=False)
+    assert c.head_dim == 192 and c.v_head_dim == 128
+    ref = oracle.case_attention(c)
+    n, S = oracle.split_plan(int(c.seq_lens.max()), positions=48)
+    o, m, l = oracle.partials(c.q, c.q_dtype, c.k_pool, c.v_pool, c.kv_dtype, c.block_table,
+                              c.seq_lens, c.softmax_scale, S, n)
+    assert o.shape == (c.rows, n, 128) and ref.shape == (c.rows, 128)
+    assert np.allclose(oracle.merge(o, m, l), ref, atol=1e-12, rtol=0)
 
 
 @pytest.mark.parametrize("split_len", [16, 48, 112, 4096])
@@ -376,8 +429,11 @@ def _pins_pass():
     o, m, l = oracle.partials(c.q, c.q_dtype, c.k_pool, c.v_pool, c.kv_dtype, c.block_table,
                               c.seq_lens, c.softmax_scale, 32, 7, causal=True)
     ok.append(np.allclose(oracle.merge(o, m, l), ref, atol=1e-10))
-    with oracle.mutation("none"):
-        pass
+    p = contiguous_problem(43, B=2, Hq=4, Hkv=2, W=1, D=16, Dv=24, lens=(35, 50))
+    try:
+        ok.append(np.allclose(oracle_on(p, 0.25), sdpa_reference(p, 0.25), atol=1e-10))
+    except ValueError:                    # a planted mistake the oracle refuses to run
+        ok.append(False)
     return all(ok), ok
 
 
@@ -386,7 +442,7 @@ def test_pins_pass_without_mutation():
 
 
 @pytest.mark.parametrize("name", ["drop_last_split", "head_mod", "causal_off_by_one",
-                                  "swap_kv", "shift_sign", "page_offset"])
+                                  "swap_kv", "shift_sign", "page_offset", "value_width"])
 def test_planted_mistake_goes_red(name):
     with oracle.mutation(name):
         passed, detail = _pins_pass()
