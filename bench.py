@@ -39,6 +39,8 @@ WORKLOAD_TEXT = {
        "K x4, append 1 then read",
     6: "ragged verify windows: 4 sequences with 16, 12, 8 and 4 causal rows, 24/4 heads, D=256, "
        "32768 keys, bf16 T=16",
+    7: "latent-attention decode: B=32, L~U[1,4096], 16/16 heads, q/k head dim 192, v head dim "
+       "128, bf16 pool T=16 shuffled, 1 query row, append 1 token per sequence first",
 }
 
 
@@ -198,7 +200,7 @@ def log(*a):
 
 def flops_of(case) -> float:
     """QK^T and PV multiply-adds over the keys each row sees (2 flops each)."""
-    D = case.head_dim
+    D = case.head_dim + case.v_head_dim
     tot = 0.0
     for b, L in enumerate(case.seq_lens.astype(np.int64)):
         W = int(case.rows_per_seq[b]) if case.rows_per_seq is not None else case.q_rows
@@ -207,7 +209,7 @@ def flops_of(case) -> float:
         else:
             keys = int(L) * W
         tot += keys
-    return tot * case.q_heads * 2 * 2 * D
+    return tot * case.q_heads * 2 * D
 
 
 def cpu_baseline(case, budget_s: float = 10.0):
@@ -233,7 +235,8 @@ def cpu_baseline(case, budget_s: float = 10.0):
                                  case.seq_lens[b:b + 1], case.softmax_scale, case.causal,
                                  case.k_scale, case.v_scale)
             t_attn += time.perf_counter() - t1
-            done_bytes += int(case.seq_lens[b]) * case.kv_heads * case.head_dim * esz * 2
+            done_bytes += (int(case.seq_lens[b]) * case.kv_heads *
+                           (case.head_dim + case.v_head_dim) * esz)
             done += 1
             if secs + t_app + t_attn >= budget_s:
                 break
@@ -256,7 +259,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5, 6])
+    ap.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush-mib", type=int, default=1024)
@@ -312,7 +315,7 @@ def main():
     else:
         n_split, split = nb.nbx_paged_decode_plan(int(case.seq_lens.max()), case.split_policy[1],
                                                   case.split_policy[2])
-    rows, D = case.rows, case.head_dim
+    rows, D = case.rows, case.v_head_dim          # partial and output columns
     o_part = torch.empty(rows, n_split, D, device=dev)
     m_part = torch.empty(rows, n_split, device=dev)
     l_part = torch.empty(rows, n_split, device=dev)
@@ -346,8 +349,11 @@ def main():
                 part_ev[1].record(stream_ptr)
                 nb.nbx_paged_decode_merge(o_ws, m_ws, l_ws, out)
             return
-        if has_append:
+        if has_append and case.head_dim == case.v_head_dim:
             nb.nbx_paged_kv_append(new_k, new_v, kp, vp, slots, dev_err=err)
+        elif has_append:                         # pools of different head dims: one call each
+            nb.nbx_paged_kv_append(new_k, None, kp, None, slots, dev_err=err)
+            nb.nbx_paged_kv_append(new_v, None, vp, None, slots, dev_err=err)
         if part_ev is not None:
             part_ev[0].record(stream_ptr)
         if windows:

@@ -13,7 +13,11 @@
  *   logical position j lives in page block_table[b, j / page_tokens] at row
  *   j % page_tokens.  New positions are written through a slot mapping,
  *   slot = page * page_tokens + row.  A query row of head h attends KV head
- *   h / (q_heads / kv_heads).  The keys are cut into splits of split_size
+ *   h / (q_heads / kv_heads).  The V rows may be narrower than the Q/K rows
+ *   (value head dim Dv independent of the query/key head dim D: nbxtensor
+ *   attention_wrappers.py, _math_attention's value head_dim, and the D_V of
+ *   the split kernel on the nbxtensor paged_decode_attn.py page); outputs
+ *   and partial outputs have Dv columns.  The keys are cut into splits of split_size
  *   positions; each split yields an unnormalised partial (o, m, l) with an
  *   fp32 accumulator, and the partials are merged in ascending split order.
  *
@@ -81,7 +85,8 @@ typedef struct {
     int32_t num_pages;
     int32_t kv_heads;
     int32_t page_tokens;    /* a multiple of 16 */
-    int32_t head_dim;       /* 64, 128 or 256 */
+    int32_t head_dim;       /* 64, 128, 192 or 256; a K / V pair of a read is
+                               (64, 64), (128, 128), (256, 256) or (192, 128) */
     int64_t stride_page;    /* elements; stride_token >= head_dim */
     int64_t stride_head;
     int64_t stride_token;
@@ -95,7 +100,10 @@ typedef struct {
  *
  *   new_k, new_v   device, [n_tok, kv_heads, head_dim] of new_dtype, element
  *                  (t, h, e) at t * new_stride_tok + h * new_stride_head + e.
- *                  new_v (and v_pool) may be null to write K only.
+ *                  new_v (and v_pool) may be null to write K only.  Both
+ *                  pools of one call have the same head_dim (else
+ *                  NBX_ERR_BAD_SHAPE): pools of different head dims are
+ *                  written by two calls, each with one pool as k_pool.
  *   new_dtype      NBX_F32 or NBX_BF16.
  *   slot_mapping   device int32 [n_tok]; slot = page * page_tokens + row.
  *                  A negative slot is skipped (padding).  A slot at or beyond
@@ -125,7 +133,8 @@ int nbx_paged_decode_plan(int32_t max_seq_len, int32_t split_positions, int32_t 
 
 /* nbx_paged_decode_workspace_bytes - host only.  Bytes of workspace that
  * nbx_paged_decode needs for `rows` query rows: the partials o [rows,
- * n_split, head_dim], m and l [rows, n_split], fp32, each 256-byte aligned. */
+ * n_split, head_dim], m and l [rows, n_split], fp32, each 256-byte aligned.
+ * head_dim is the V pool's (the width of o). */
 size_t nbx_paged_decode_workspace_bytes(int64_t rows, int32_t n_split, int32_t head_dim);
 
 /*
@@ -140,7 +149,9 @@ size_t nbx_paged_decode_workspace_bytes(int64_t rows, int32_t n_split, int32_t h
  *                1: row r sees keys [0, seq_lens[b] - q_rows + r], i.e. the
  *                q_rows rows are the last q_rows positions of the sequence,
  *                already in the pool.
- *   k_pool/v_pool  same dtype, num_pages, kv_heads, page_tokens, head_dim.
+ *   k_pool/v_pool  same dtype, num_pages, kv_heads, page_tokens; head dims
+ *                D (of q and K) and Dv (of V) one of the pairs listed at
+ *                nbx_kv_pool.  q is [.., D]; o_part and the output [.., Dv].
  *   block_table  device int32 [batch, max_pages] (row stride max_pages), -1
  *                past each sequence.  Entries covering [0, seq_lens[b]) must
  *                lie in [0, num_pages); a violation sets NBX_DEVERR_PAGE_RANGE
@@ -157,7 +168,7 @@ size_t nbx_paged_decode_workspace_bytes(int64_t rows, int32_t n_split, int32_t h
  *                (the split kernel's rule on the nbxtensor paged_decode_attn.py
  *                page), so a launch recorded in a graph stays right as the
  *                lengths grow; n_split then only bounds the split count.
- *   o_part       device fp32 [rows, n_split, head_dim]: sum_j exp(s_j - m) v_j
+ *   o_part       device fp32 [rows, n_split, Dv]: sum_j exp(s_j - m) v_j
  *   m_part       device fp32 [rows, n_split]: max_j s_j (natural-log units)
  *   l_part       device fp32 [rows, n_split]: sum_j exp(s_j - m)
  *                where s_j = scale * pool.scale_k * (q . k_j) over the split.
@@ -209,7 +220,8 @@ int nbx_paged_decode_partial_windows(const void *q, int32_t q_dtype, int32_t bat
  *
  *   o_part, m_part, l_part  as written by nbx_paged_decode_partial.
  *   out          device [rows, head_dim] of out_dtype (NBX_F32 or NBX_BF16,
- *                bf16 rounded to nearest even).
+ *                bf16 rounded to nearest even); head_dim is the partials'
+ *                width Dv, 64, 128 or 256.
  *   n_split      at most 4096, else NBX_ERR_UNSUPPORTED.
  */
 int nbx_paged_decode_merge(const float *o_part, const float *m_part, const float *l_part,
@@ -220,7 +232,8 @@ int nbx_paged_decode_merge(const float *o_part, const float *m_part, const float
  * nbx_paged_decode - partial then merge on one stream (nbxtensor
  * attention_wrappers.py, paged_decode_attention).  Arguments as for the two
  * calls; `workspace` (device, at least nbx_paged_decode_workspace_bytes(rows,
- * n_split, head_dim) bytes, 256-byte aligned) holds the partials.
+ * n_split, Dv) bytes, 256-byte aligned) holds the partials; out is
+ * [batch, q_heads, q_rows, Dv].
  */
 int nbx_paged_decode(const void *q, int32_t q_dtype, int32_t batch, int32_t q_heads,
                      int32_t q_rows, int32_t causal, const nbx_kv_pool *k_pool,
@@ -247,9 +260,10 @@ int nbx_paged_decode(const void *q, int32_t q_dtype, int32_t batch, int32_t q_he
  * kernel launch; otherwise the append, partial and merge kernels run in turn
  * on `stream`.
  *
- *   new_k, new_v   device, [batch, n_new, kv_heads, head_dim] contiguous, of
- *                  new_dtype (NBX_F32 or NBX_BF16); stored with the
- *                  conversions of nbx_paged_kv_append.  Ignored if n_new == 0.
+ *   new_k, new_v   device, new_k [batch, n_new, kv_heads, D] and new_v
+ *                  [batch, n_new, kv_heads, Dv], contiguous, of new_dtype
+ *                  (NBX_F32 or NBX_BF16); stored with the conversions of
+ *                  nbx_paged_kv_append.  Ignored if n_new == 0.
  *   n_new          new positions per sequence (>= 0).  A sequence shorter
  *                  than n_new sets NBX_DEVERR_SEQ_RANGE and its tokens that
  *                  would land before position 0 are skipped; a block-table
@@ -257,7 +271,7 @@ int nbx_paged_decode(const void *q, int32_t q_dtype, int32_t batch, int32_t q_he
  *                  token is skipped.  The slots of the new positions must not
  *                  be read by another sequence of the same call.
  *   workspace      as for nbx_paged_decode.  It holds the partials afterwards:
- *                  o at offset 0, m at round256(rows * n_split * head_dim * 4),
+ *                  o at offset 0, m at round256(rows * n_split * Dv * 4),
  *                  l after m at round256(rows * n_split * 4), the layouts of
  *                  nbx_paged_decode_partial (round256 = next multiple of 256).
  *   out            may be null: the step then stops after the partials (for a

@@ -205,9 +205,9 @@ def nbx_paged_decode_partial(q, k_pool: KVPool, v_pool: KVPool, block_table, seq
                              scale: float, split_size: int, n_split: int, o_part, m_part, l_part,
                              causal: bool = False, dev_err=None, stream=None):
     kd, vd = _decode_common(q, k_pool, v_pool, block_table, seq_lens)
-    B, Hq, W, D = q.shape
-    rows = B * Hq * W
-    for name, t, shape in (("o_part", o_part, (rows, n_split, D)), ("m_part", m_part, (rows, n_split)),
+    B, Hq, W, _ = q.shape
+    rows, Dv = B * Hq * W, v_pool.data.shape[3]
+    for name, t, shape in (("o_part", o_part, (rows, n_split, Dv)), ("m_part", m_part, (rows, n_split)),
                            ("l_part", l_part, (rows, n_split))):
         if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous fp32 {shape}")
@@ -232,11 +232,13 @@ def nbx_paged_decode(q, k_pool: KVPool, v_pool: KVPool, block_table, seq_lens, s
                      split_size: int, n_split: int, workspace, out, causal: bool = False,
                      dev_err=None, stream=None):
     """One call: partial then merge; ``workspace`` a uint8 device tensor of at least
-    nbx_paged_decode_workspace_bytes(rows, n_split, head_dim) bytes."""
+    nbx_paged_decode_workspace_bytes(rows, n_split, v_head_dim) bytes; ``out`` is
+    [batch, q_heads, q_rows, v_head_dim]."""
     kd, vd = _decode_common(q, k_pool, v_pool, block_table, seq_lens)
-    B, Hq, W, D = q.shape
-    if out.numel() != B * Hq * W * D or not out.is_contiguous():
-        raise ValueError("out must be contiguous [batch, q_heads, q_rows, head_dim]")
+    B, Hq, W, _ = q.shape
+    Dv = v_pool.data.shape[3]
+    if out.numel() != B * Hq * W * Dv or not out.is_contiguous():
+        raise ValueError("out must be contiguous [batch, q_heads, q_rows, v_head_dim]")
     st = load_library().nbx_paged_decode(
         _ptr(q), _dtype_code(q), B, Hq, W, int(bool(causal)), ctypes.byref(kd), ctypes.byref(vd),
         _ptr(block_table), block_table.shape[1], _ptr(seq_lens), float(scale), int(split_size),
@@ -248,21 +250,25 @@ def nbx_paged_decode(q, k_pool: KVPool, v_pool: KVPool, block_table, seq_lens, s
 def nbx_paged_decode_step(q, k_pool: KVPool, v_pool: KVPool, block_table, seq_lens, scale: float,
                           split_size: int, n_split: int, workspace, out, new_k=None, new_v=None,
                           causal: bool = False, dev_err=None, stream=None):
-    """One decode step: new_k / new_v [batch, n_new, kv_heads, head_dim] (fp32 or bf16,
-    contiguous) written at each sequence's last n_new positions, then partial and merge.
-    ``seq_lens`` count the new positions; ``workspace`` as for nbx_paged_decode.  With
-    ``out=None`` the step stops after the partials, which stay in the workspace."""
+    """One decode step: new_k [batch, n_new, kv_heads, head_dim] and new_v [batch, n_new,
+    kv_heads, v_head_dim] (fp32 or bf16, contiguous) written at each sequence's last n_new
+    positions, then partial and merge.  ``seq_lens`` count the new positions; ``workspace``
+    as for nbx_paged_decode.  With ``out=None`` the step stops after the partials, which
+    stay in the workspace."""
     kd, vd = _decode_common(q, k_pool, v_pool, block_table, seq_lens)
     B, Hq, W, D = q.shape
-    if out is not None and (out.numel() != B * Hq * W * D or not out.is_contiguous()):
-        raise ValueError("out must be contiguous [batch, q_heads, q_rows, head_dim]")
+    Dv = v_pool.data.shape[3]
+    if out is not None and (out.numel() != B * Hq * W * Dv or not out.is_contiguous()):
+        raise ValueError("out must be contiguous [batch, q_heads, q_rows, v_head_dim]")
     n_new, new_dt = 0, 0
     if new_k is not None:
-        if new_v is None or new_k.shape != new_v.shape or new_k.dtype != new_v.dtype:
+        if new_v is None or new_k.shape[:3] != new_v.shape[:3] or new_k.dtype != new_v.dtype:
             raise ValueError("new_k and new_v must match")
         if new_k.dim() != 4 or new_k.shape[0] != B or new_k.shape[2] != k_pool.data.shape[1] \
-                or new_k.shape[3] != D or not (new_k.is_contiguous() and new_v.is_contiguous()):
-            raise ValueError("new_k / new_v must be contiguous [batch, n_new, kv_heads, head_dim]")
+                or new_k.shape[3] != D or new_v.shape[3] != Dv \
+                or not (new_k.is_contiguous() and new_v.is_contiguous()):
+            raise ValueError("new_k / new_v must be contiguous [batch, n_new, kv_heads, "
+                             "head_dim / v_head_dim]")
         n_new, new_dt = new_k.shape[1], _dtype_code(new_k)
     st = load_library().nbx_paged_decode_step(
         _ptr(q), _dtype_code(q), B, Hq, W, int(bool(causal)), _ptr(new_k), _ptr(new_v), new_dt,

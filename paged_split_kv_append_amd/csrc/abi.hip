@@ -17,7 +17,17 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool dtype_ok(int32_t d) { return d == NBX_F32 || d == NBX_BF16 || d == NBX_FP8_E4M3; }
 
-bool head_dim_ok(int32_t d) { return d == 64 || d == 128 || d == 256; }
+// head dims of one pool; a V pool's (the partial and output width) is one of
+// 64, 128, 256
+bool head_dim_ok(int32_t d) { return d == 64 || d == 128 || d == 192 || d == 256; }
+bool value_dim_ok(int32_t d) { return d == 64 || d == 128 || d == 256; }
+
+// (q/k head dim, v head dim) pairs the partial kernels are built for: equal
+// dims, or the latent-attention pair 192 / 128
+bool head_dims_ok(int32_t dk, int32_t dv)
+{
+    return (dk == dv && value_dim_ok(dk)) || (dk == 192 && dv == 128);
+}
 
 // geometry and alignment of one pool; returns NBX_OK or an error
 int check_pool(const nbx_kv_pool *p)
@@ -40,10 +50,11 @@ int check_pool(const nbx_kv_pool *p)
     return NBX_OK;
 }
 
-bool same_geometry(const nbx_kv_pool *a, const nbx_kv_pool *b)
+// the same pages, heads, positions and element type (head dims checked apart)
+bool same_layout(const nbx_kv_pool *a, const nbx_kv_pool *b)
 {
     return a->dtype == b->dtype && a->num_pages == b->num_pages && a->kv_heads == b->kv_heads &&
-           a->page_tokens == b->page_tokens && a->head_dim == b->head_dim;
+           a->page_tokens == b->page_tokens;
 }
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -127,7 +138,9 @@ int nbx_paged_kv_append(const void *new_k, const void *new_v, int32_t new_dtype,
     if (v_pool) {
         if ((st = check_pool(v_pool)) != NBX_OK)
             return st;
-        if (!same_geometry(k_pool, v_pool))
+        // one pair of source strides serves both: pools of different head
+        // dims are appended in two calls
+        if (!same_layout(k_pool, v_pool) || k_pool->head_dim != v_pool->head_dim)
             return NBX_ERR_BAD_SHAPE;
     }
     if (n_tok < 0 || new_stride_head < k_pool->head_dim || new_stride_tok < 0)
@@ -150,6 +163,9 @@ int nbx_paged_kv_append(const void *new_k, const void *new_v, int32_t new_dtype,
     a.new_stride_head = new_stride_head;
     a.kv_heads = k_pool->kv_heads;
     a.head_dim = k_pool->head_dim;
+    a.v_head_dim = k_pool->head_dim;
+    a.v_new_stride_tok = new_stride_tok;
+    a.v_new_stride_head = new_stride_head;
     a.num_pages = k_pool->num_pages;
     a.page_tokens = k_pool->page_tokens;
     a.k_data = k_pool->data;
@@ -184,7 +200,7 @@ static int validate_partial(const void *q, int32_t q_dtype, int32_t batch, int32
         return st;
     if ((st = check_pool(v_pool)) != NBX_OK)
         return st;
-    if (!same_geometry(k_pool, v_pool))
+    if (!same_layout(k_pool, v_pool) || !head_dims_ok(k_pool->head_dim, v_pool->head_dim))
         return NBX_ERR_BAD_SHAPE;
     if (batch < 0 || q_heads < 1 || q_rows < 1 || max_pages < 1 || (causal != 0 && causal != 1))
         return NBX_ERR_BAD_SHAPE;
@@ -225,6 +241,7 @@ static nbx::PartialArgs partial_args(const void *q, int32_t q_dtype, int32_t bat
     a.group = q_heads / k_pool->kv_heads;
     a.rows_per_kv = a.group * q_rows;
     a.head_dim = k_pool->head_dim;
+    a.v_head_dim = v_pool->head_dim;
     a.num_pages = k_pool->num_pages;
     a.page_tokens = k_pool->page_tokens;
     a.k_data = k_pool->data;
@@ -326,7 +343,7 @@ int nbx_paged_decode_merge(const float *o_part, const float *m_part, const float
         return NBX_ERR_NULL_PTR;
     if (out_dtype != NBX_F32 && out_dtype != NBX_BF16)
         return NBX_ERR_BAD_DTYPE;
-    if (rows < 0 || n_split < 1 || !head_dim_ok(head_dim))
+    if (rows < 0 || n_split < 1 || !value_dim_ok(head_dim))
         return NBX_ERR_BAD_SHAPE;
     if (n_split > kMaxMergeSplits)
         return NBX_ERR_UNSUPPORTED;
@@ -359,20 +376,20 @@ int nbx_paged_decode(const void *q, int32_t q_dtype, int32_t batch, int32_t q_he
     if (batch == 0)
         return NBX_OK;
     const int64_t rows = (int64_t)batch * q_heads * q_rows;
-    const int32_t D = k_pool->head_dim;
-    const size_t need = nbx_paged_decode_workspace_bytes(rows, n_split, D);
+    const int32_t Dv = v_pool->head_dim;      // partial and output columns
+    const size_t need = nbx_paged_decode_workspace_bytes(rows, n_split, Dv);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
         return NBX_ERR_WORKSPACE;
     char *ws = (char *)workspace;
     float *o_part = (float *)ws;
-    float *m_part = (float *)(ws + round256((size_t)rows * n_split * D * sizeof(float)));
+    float *m_part = (float *)(ws + round256((size_t)rows * n_split * Dv * sizeof(float)));
     float *l_part = (float *)((char *)m_part + round256((size_t)rows * n_split * sizeof(float)));
     st = nbx_paged_decode_partial(q, q_dtype, batch, q_heads, q_rows, causal, k_pool, v_pool,
                                   block_table, max_pages, seq_lens, scale, split_size, n_split,
                                   o_part, m_part, l_part, dev_err, stream);
     if (st != NBX_OK)
         return st;
-    return nbx_paged_decode_merge(o_part, m_part, l_part, rows, n_split, D, out, out_dtype,
+    return nbx_paged_decode_merge(o_part, m_part, l_part, rows, n_split, Dv, out, out_dtype,
                                   stream);
 }
 
@@ -401,7 +418,7 @@ int nbx_paged_decode_step(const void *q, int32_t q_dtype, int32_t batch, int32_t
         if (!aligned16(new_k) || !aligned16(new_v))
             return NBX_ERR_BAD_ALIGN;
         if ((int64_t)batch * n_new * k_pool->kv_heads * (k_pool->head_dim / 8) >
-            (int64_t)INT32_MAX * 256)
+            (int64_t)INT32_MAX * 256)      // the wider of the K and V rows
             return NBX_ERR_BAD_SHAPE;
     }
     if (n_split > kMaxMergeSplits)
@@ -411,13 +428,13 @@ int nbx_paged_decode_step(const void *q, int32_t q_dtype, int32_t batch, int32_t
     if (batch == 0)
         return NBX_OK;
     const int64_t rows = (int64_t)batch * q_heads * q_rows;
-    const int32_t D = k_pool->head_dim;
-    const size_t need = nbx_paged_decode_workspace_bytes(rows, n_split, D);
+    const int32_t D = k_pool->head_dim, Dv = v_pool->head_dim;
+    const size_t need = nbx_paged_decode_workspace_bytes(rows, n_split, Dv);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
         return NBX_ERR_WORKSPACE;
     char *ws = (char *)workspace;
     float *o_part = (float *)ws;
-    float *m_part = (float *)(ws + round256((size_t)rows * n_split * D * sizeof(float)));
+    float *m_part = (float *)(ws + round256((size_t)rows * n_split * Dv * sizeof(float)));
     float *l_part = (float *)((char *)m_part + round256((size_t)rows * n_split * sizeof(float)));
     nbx::PartialArgs a =
         partial_args(q, q_dtype, batch, q_heads, q_rows, causal, k_pool, v_pool, block_table,
@@ -443,6 +460,9 @@ int nbx_paged_decode_step(const void *q, int32_t q_dtype, int32_t batch, int32_t
             ap.new_stride_head = D;
             ap.kv_heads = k_pool->kv_heads;
             ap.head_dim = D;
+            ap.v_head_dim = Dv;
+            ap.v_new_stride_tok = (int64_t)k_pool->kv_heads * Dv;
+            ap.v_new_stride_head = Dv;
             ap.num_pages = k_pool->num_pages;
             ap.page_tokens = k_pool->page_tokens;
             ap.k_data = k_pool->data;
@@ -470,7 +490,7 @@ int nbx_paged_decode_step(const void *q, int32_t q_dtype, int32_t batch, int32_t
         return NBX_ERR_LAUNCH;
     if (!out)
         return NBX_OK;                         // partials only, left in the workspace
-    nbx::MergeArgs m{o_part, m_part, l_part, rows, n_split, D, out, out_dtype};
+    nbx::MergeArgs m{o_part, m_part, l_part, rows, n_split, Dv, out, out_dtype};
     return to_status(nbx::launch_merge(m, stream));
 }
 

@@ -8,7 +8,7 @@
 //
 // One thread moves 8 consecutive elements of one (token, KV head) row, so a
 // row of D elements takes D/8 threads and the K and V pools are written by
-// the same launch (blockIdx.y selects K or V).
+// the same launch (blockIdx.y selects K or V; V rows may be narrower).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -69,12 +69,12 @@ template <int SRC, int DST>
 __global__ void __launch_bounds__(256)
 paged_append_kernel(AppendArgs a)
 {
-    const int64_t chunks_per_row = a.head_dim / 8;
+    const bool is_v = blockIdx.y == 1;
+    const int64_t chunks_per_row = (is_v ? a.v_head_dim : a.head_dim) / 8;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t total = a.n_tok * a.kv_heads * chunks_per_row;
     if (gid >= total)
         return;
-    const bool is_v = blockIdx.y == 1;
     const void *src = is_v ? a.new_v : a.new_k;
     void *pool = is_v ? a.v_data : a.k_data;
     const int64_t sp = is_v ? a.v_stride_page : a.k_stride_page;
@@ -116,7 +116,8 @@ paged_append_kernel(AppendArgs a)
     }
     const int64_t page = slot / a.page_tokens;
     const int64_t row = slot - page * a.page_tokens;
-    const int64_t si = t * a.new_stride_tok + h * a.new_stride_head + c * 8;
+    const int64_t si = t * (is_v ? a.v_new_stride_tok : a.new_stride_tok) +
+                       h * (is_v ? a.v_new_stride_head : a.new_stride_head) + c * 8;
     const int64_t di = page * sp + h * sh + row * st + c * 8;
     float x[8];
     load8<SRC>(src, si, x);
@@ -126,7 +127,8 @@ paged_append_kernel(AppendArgs a)
 template <int SRC, int DST>
 static hipError_t launch_append_t(const AppendArgs &a, hipStream_t stream)
 {
-    const int64_t total = a.n_tok * a.kv_heads * (a.head_dim / 8);
+    const int32_t widest = a.new_v && a.v_head_dim > a.head_dim ? a.v_head_dim : a.head_dim;
+    const int64_t total = a.n_tok * a.kv_heads * (widest / 8);
     dim3 grid((unsigned)((total + 255) / 256), a.new_v ? 2 : 1);
     hipLaunchKernelGGL((paged_append_kernel<SRC, DST>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();

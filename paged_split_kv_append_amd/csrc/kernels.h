@@ -14,6 +14,10 @@ struct AppendArgs {
     int32_t src_dtype, dst_dtype;
     int64_t n_tok, new_stride_tok, new_stride_head;
     int32_t kv_heads, head_dim, num_pages, page_tokens;
+    // V rows: their own head dim and source strides (the same as K's unless the
+    // V pool's head dim differs)
+    int32_t v_head_dim;
+    int64_t v_new_stride_tok, v_new_stride_head;
     void *k_data;
     int64_t k_stride_page, k_stride_head, k_stride_token;
     void *v_data;
@@ -34,6 +38,7 @@ struct PartialArgs {
     int32_t kv_heads, group;        // group = q_heads / kv_heads
     int32_t rows_per_kv;            // group * q_rows: rows sharing one KV head
     int32_t head_dim, num_pages, page_tokens;
+    int32_t v_head_dim;             // Dv: V rows, partial and output columns
     const void *k_data;
     int64_t k_stride_page, k_stride_head, k_stride_token;
     const void *v_data;
@@ -49,8 +54,9 @@ struct PartialArgs {
     // ragged windows: rows of sequence b (null: q_rows for every sequence)
     const int32_t *rows_per_seq;
     // single-launch step (persistent decode kernel): the n_new new positions
-    // of each sequence, [batch, n_new, kv_heads, head_dim] of new_dtype, are
-    // written by the wave that owns the item holding them
+    // of each sequence, new_k [batch, n_new, kv_heads, head_dim] and new_v
+    // [batch, n_new, kv_heads, v_head_dim] of new_dtype, are written by the
+    // wave that owns the item holding them
     const void *new_k, *new_v;
     int32_t new_dtype, n_new;
 };

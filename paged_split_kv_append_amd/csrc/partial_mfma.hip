@@ -12,6 +12,8 @@
 // Products are v_mfma_f32_16x16x32_bf16 with fp32 accumulation:
 //   S^T (16 positions x 16 rows) = K (16 x D) . Q^T (D x 16)
 //   O^T (16 columns x 16 rows) += V^T (16 x 32 positions) . P^T (32 x 16)
+// D is the q/k head dim and DV the V head dim (the width of o; the two differ
+// for latent-attention heads, e.g. 192 / 128).
 // so that every lane owns one query row (its column) in both S^T and O^T and
 // the softmax bookkeeping never leaves the lane's row.  bf16 K/V products are
 // exact; P is rounded to bf16 for the P V product, and for bf16 pools the
@@ -225,16 +227,16 @@ __device__ __forceinline__ void softmax_step(float (&sc)[2][4], float &m_run, fl
 
 // ------------------------------------------------------------------ decode
 
-template <int D, int KVT, bool PVS, int PG>
+template <int D, int DV, int KVT, bool PVS, int PG>
 __global__ void __launch_bounds__(PG * 64)
 decode_mfma_kernel(PartialArgs a)
 {
     constexpr int KK = D / 32;                 // 32-wide k-steps of Q K^T
-    constexpr int DT = D / 16;                 // 16-column slices of V and O
+    constexpr int DT = DV / 16;                // 16-column slices of V and O
     constexpr bool BF = KVT == NBX_BF16;
     constexpr int ESZ = BF ? 2 : 1;
-    constexpr int VBYTES = kChunk * 2 * D;     // one chunk of V as bf16
-    constexpr int CMB = PG > 1 ? PG * 16 * D * 4 : 0;
+    constexpr int VBYTES = kChunk * 2 * DV;    // one chunk of V as bf16
+    constexpr int CMB = PG > 1 ? PG * 16 * DV * 4 : 0;
     constexpr int SMEM = (PG * VBYTES > CMB) ? PG * VBYTES : CMB;
     __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
     __shared__ float cmb_m[PG][16], cmb_l[PG][16];
@@ -400,7 +402,7 @@ decode_mfma_kernel(PartialArgs a)
     if constexpr (PG == 1) {
         if (j < M) {
             const int64_t row = row_base + j;
-            float *op = a.o_part + (row * a.n_split + s) * D;
+            float *op = a.o_part + (row * a.n_split + s) * DV;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
                 *(f32x4 *)(op + dt * 16 + 4 * g) = o[dt] * vs;
@@ -418,10 +420,10 @@ decode_mfma_kernel(PartialArgs a)
         }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-            *(f32x4 *)(cmb_o + (w * 16 + j) * D + dt * 16 + 4 * g) = o[dt] * vs;
+            *(f32x4 *)(cmb_o + (w * 16 + j) * DV + dt * 16 + 4 * g) = o[dt] * vs;
         __syncthreads();
-        for (int idx = threadIdx.x; idx < M * D; idx += PG * 64) {
-            const int r = idx / D, e = idx % D;
+        for (int idx = threadIdx.x; idx < M * DV; idx += PG * 64) {
+            const int r = idx / DV, e = idx % DV;
             float mx = -INFINITY;
 #pragma unroll
             for (int k = 0; k < PG; ++k)
@@ -434,12 +436,12 @@ decode_mfma_kernel(PartialArgs a)
                     if (mk == -INFINITY)
                         continue;
                     const float f = fast_exp2(mk - mx);
-                    ov = fmaf(f, cmb_o[(k * 16 + r) * D + e], ov);
+                    ov = fmaf(f, cmb_o[(k * 16 + r) * DV + e], ov);
                     lv = fmaf(f, cmb_l[k][r], lv);
                 }
             }
             const int64_t row = row_base + r;
-            a.o_part[(row * a.n_split + s) * D + e] = ov;
+            a.o_part[(row * a.n_split + s) * DV + e] = ov;
             if (e == 0) {
                 a.m_part[row * a.n_split + s] = mx == -INFINITY ? -INFINITY : mx * kLn2;
                 a.l_part[row * a.n_split + s] = lv;
@@ -489,14 +491,14 @@ constexpr int kPersistMaxBatch = 256;      // sequences covered by the lane-regi
 // and page ids) in flight while the current chunk is computed, so the cost of
 // starting a wave is paid once, not once per split.  Splits without keys get
 // m = -inf and l = 0; their o is not written.
-template <int D, int KVT, bool PVS, int NB, bool FA>
+template <int D, int DV, int KVT, bool PVS, int NB, bool FA>
 __global__ void __launch_bounds__(64)
 decode_persistent_kernel(PartialArgs a)
 {
-    constexpr int KK = D / 32, DT = D / 16;
+    constexpr int KK = D / 32, DT = DV / 16;
     constexpr bool BF = KVT == NBX_BF16;
     constexpr int ESZ = BF ? 2 : 1;
-    constexpr int VBYTES = kChunk * 2 * D;
+    constexpr int VBYTES = kChunk * 2 * DV;
     __shared__ __attribute__((aligned(16))) uint8_t tile[VBYTES];
 
     const int lane = threadIdx.x;
@@ -624,16 +626,16 @@ decode_persistent_kernel(PartialArgs a)
                                          : tile_page(a, it.b, p, hi, lane == 0);
                 if (page < 0)
                     continue;
-                const int64_t src = (((int64_t)it.b * a.n_new + (p - first)) * H + it.gk) * D;
+                const int64_t src = ((int64_t)it.b * a.n_new + (p - first)) * H + it.gk;
                 const int64_t r = p % a.page_tokens;
-                store_new_row<D, KVT>(a.new_k, a.new_dtype, src, (void *)a.k_data,
+                store_new_row<D, KVT>(a.new_k, a.new_dtype, src * D, (void *)a.k_data,
                                       (int64_t)page * a.k_stride_page + it.gk * a.k_stride_head +
                                           r * a.k_stride_token,
                                       a.k_scale, lane);
-                store_new_row<D, KVT>(a.new_v, a.new_dtype, src, (void *)a.v_data,
-                                      (int64_t)page * a.v_stride_page + it.gk * a.v_stride_head +
-                                          r * a.v_stride_token,
-                                      a.v_scale, lane);
+                store_new_row<DV, KVT>(a.new_v, a.new_dtype, src * DV, (void *)a.v_data,
+                                       (int64_t)page * a.v_stride_page + it.gk * a.v_stride_head +
+                                           r * a.v_stride_token,
+                                       a.v_scale, lane);
             }
             asm volatile("" ::: "memory");     // keep the tile loads after the stores
         }
@@ -794,7 +796,7 @@ decode_persistent_kernel(PartialArgs a)
             const float lt = xor_sum16_32(l_run);
             if (j < M) {
                 const int64_t row = ci.row_base + j;
-                float *op = a.o_part + (row * NS + ci.s) * D;
+                float *op = a.o_part + (row * NS + ci.s) * DV;
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt)
                     *(f32x4 *)(op + dt * 16 + 4 * g) = o[dt] * vs;
@@ -817,15 +819,15 @@ decode_persistent_kernel(PartialArgs a)
 // ------------------------------------------------------------------ multi-row
 
 // A workgroup of 8 waves takes 8 x NT row tiles of 16 rows of one (sequence,
-// KV head, split).  The 2 K tiles and 2 V tiles of a 32-position chunk are
-// 2 KK + DT pieces of 1 KB (as bf16); wave w loads pieces w, w + 8, ..., so
-// for D = 256 each of its loads has a fixed role (K or V, tile) and one
-// descriptor per tile serves the whole workgroup.  Chunk c + 1 waits in LDS
+// KV head, split).  The K and V tiles of a chunk are pieces of 1 KB (as bf16:
+// 16 rows x 32 columns); waves 0-3 load the K pieces and waves 4-7 the V
+// pieces, each wave all its pieces from one tile, so each of its loads has a
+// fixed role (K or V, tile) and one descriptor per tile serves it.  Chunk c + 1 waits in LDS
 // and chunks c + 2, c + 3 in registers while chunk c is computed; one barrier
 // per chunk.  K is stored in LDS with a 16-byte swizzle inside each 1 KB
 // block (row r, piece p at unit 4 r + ((p + r / 4) & 3)), so that the 16
 // lanes of a group reading one 16-byte operand piece each cover all banks.
-template <int D, int KVT, bool PVS, int NT, int NK, int NSET>
+template <int D, int DV, int KVT, bool PVS, int NT, int NK, int NSET>
 __global__ void __launch_bounds__(512)
 multirow_mfma_kernel(PartialArgs a, int row_blocks)
 {
@@ -833,15 +835,18 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
     constexpr int CH = 32 * NK;                // positions per chunk (NK k-steps of P V)
     constexpr int TL = 2 * NK;                 // 16-position tiles per chunk
     constexpr int BATCH = 64 / TL;             // chunks whose tiles fill one lane register
-    constexpr int KK = D / 32, DT = D / 16;
+    constexpr int KK = D / 32, DT = DV / 16;
+    constexpr int KV = DV / 32;                // 32-column V pieces per tile
     constexpr bool BF = KVT == NBX_BF16;
     constexpr int ESZ = BF ? 2 : 1;
     constexpr int KBYTES = CH * 2 * D;         // K chunk as bf16: [tile][KK][16 rows][64 B]
-    constexpr int VBYTES = CH * 2 * D;         // V chunk as bf16: [tile][DT][16 rows][32 B]
+    constexpr int VBYTES = CH * 2 * DV;        // V chunk as bf16: [tile][DT][16 rows][32 B]
     constexpr int BUF = KBYTES + VBYTES;
-    constexpr int NI = TL * 2 * KK;            // 1 KB (bf16) pieces per chunk: K then V
-    constexpr int PER = NI / RW;               // pieces per wave
-    static_assert(PER <= KK && KK % PER == 0, "a wave's pieces lie in one tile");
+    // pieces per wave: TL x KK of K over waves 0-3, TL x KV of V over waves 4-7
+    constexpr int PER_K = TL * KK / 4, PER_V = TL * KV / 4;
+    constexpr int PMAX = PER_K > PER_V ? PER_K : PER_V;
+    static_assert(PER_K <= KK && KK % PER_K == 0 && PER_V <= KV && KV % PER_V == 0,
+                  "a wave's pieces lie in one tile");
     constexpr int R = RW * NT * 16;            // rows per workgroup
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF];
 
@@ -914,12 +919,13 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
     const uint8_t *k_rd = smem + (4 * j + ((g + (j >> 2)) & 3)) * 16;   // + (t*KK + kk) * 1024
     const uint8_t *vt_lane = smem + KBYTES + (4 * g + (j >> 2)) * 32 + (j & 3) * 8;
 
-    // Wave roles: waves 0-3 load K, 4-7 load V; of the TL x KK pieces of its
-    // pool (tile-major: K 32-column groups kk, V 32-column pairs of 16-column
-    // slices) wave w takes (w & 3) * PER ... (w & 3) * PER + PER - 1, all in
+    // Wave roles: waves 0-3 load K, 4-7 load V; of the pieces of its pool
+    // (tile-major: K 32-column groups kk, V 32-column pairs of 16-column
+    // slices) wave w takes (w & 3) * per ... (w & 3) * per + per - 1, all in
     // tile t_w of every chunk.
     const bool is_k = w < 4;
-    const int t_w = ((w & 3) * PER) / KK, pbase = ((w & 3) * PER) % KK;
+    const int per = is_k ? PER_K : PER_V, pieces = is_k ? KK : KV;
+    const int t_w = ((w & 3) * per) / pieces, pbase = ((w & 3) * per) % pieces;
     const uint8_t *role_base = is_k ? (const uint8_t *)a.k_data + k_head * ESZ
                                     : (const uint8_t *)a.v_data + v_head * ESZ;
     const int64_t role_sp = (is_k ? a.k_stride_page : a.v_stride_page) * ESZ;
@@ -962,8 +968,8 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
     };
 
     struct Regs {
-        u32x4 r16[BF ? PER : 1];
-        u32x2 r8[BF ? 1 : PER];
+        u32x4 r16[BF ? PMAX : 1];
+        u32x2 r8[BF ? 1 : PMAX];
     };
     // this wave's pieces of chunk c into registers: one descriptor per chunk
     auto issue = [&](int c, Regs &rg) {
@@ -973,7 +979,9 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
         const uint32_t nb = __builtin_amdgcn_readlane(q ? nbytes1 : nbytes0, li);
         const i32x4 rs = make_buffer_rsrc(role_base + (((uint64_t)hi << 32) | lo), nb);
 #pragma unroll
-        for (int x = 0; x < PER; ++x) {
+        for (int x = 0; x < PMAX; ++x) {
+            if (x >= per)                      // (never taken when K and V widths match)
+                break;
             if constexpr (BF)
                 rg.r16[x] = nbx_buffer_load_b128(rs, role_lane + x * 32 * ESZ, 0, 0);
             else
@@ -986,7 +994,9 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
         uint8_t *dst = is_k ? buf + (t_w * KK + pbase) * 1024 + k_st
                             : buf + KBYTES + t_w * DT * 512 + pbase * 1024 + lane * 16;
 #pragma unroll
-        for (int x = 0; x < PER; ++x) {
+        for (int x = 0; x < PMAX; ++x) {
+            if (x >= per)
+                break;
             if constexpr (BF)
                 *(u32x4 *)(dst + x * 1024) = rg.r16[x];
             else
@@ -1082,7 +1092,7 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
         const int m = row_lo + (w * NT + n) * 16 + j;
         if (m < row_hi) {
             const int64_t row = row_base + m;
-            float *op = a.o_part + (row * a.n_split + s) * D;
+            float *op = a.o_part + (row * a.n_split + s) * DV;
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt)
                 *(f32x4 *)(op + dt * 16 + 4 * g) = o[n][dt] * vs;
@@ -1102,7 +1112,7 @@ constexpr int kMrNK = 2, kMrNSet = 1;
 
 // Waves the current device holds at once for the persistent decode kernel
 // (resident workgroups per CU x CUs), cached per device.
-template <int D, int KVT, bool PVS, int NB, bool FA>
+template <int D, int DV, int KVT, bool PVS, int NB, bool FA>
 int persistent_waves()
 {
     constexpr int kMaxDev = 64;
@@ -1117,7 +1127,8 @@ int persistent_waves()
     }
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void *>(&decode_persistent_kernel<D, KVT, PVS, NB, FA>), 64,
+            &per_cu,
+            reinterpret_cast<const void *>(&decode_persistent_kernel<D, DV, KVT, PVS, NB, FA>), 64,
             0) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
@@ -1127,16 +1138,16 @@ int persistent_waves()
     return v;
 }
 
-template <int D, int KVT, bool PVS, int NB, bool FA>
+template <int D, int DV, int KVT, bool PVS, int NB, bool FA>
 hipError_t launch_persistent(const PartialArgs &a, hipStream_t stream)
 {
     const int64_t items = (int64_t)a.batch * a.kv_heads * a.n_split;
-    const int waves = persistent_waves<D, KVT, PVS, NB, FA>();
+    const int waves = persistent_waves<D, DV, KVT, PVS, NB, FA>();
     if (waves <= 0)
         return hipErrorInvalidConfiguration;
     const int grid = (int)(items < waves ? items : waves);
-    hipLaunchKernelGGL((decode_persistent_kernel<D, KVT, PVS, NB, FA>), dim3(grid), dim3(64), 0,
-                       stream, a);
+    hipLaunchKernelGGL((decode_persistent_kernel<D, DV, KVT, PVS, NB, FA>), dim3(grid), dim3(64),
+                       0, stream, a);
     return hipGetLastError();
 }
 
@@ -1145,17 +1156,17 @@ bool persistent_shape(const PartialArgs &a)
     return a.rows_per_kv <= 16 && a.batch <= kPersistMaxBatch;
 }
 
-template <int D, int KVT, bool PVS>
+template <int D, int DV, int KVT, bool PVS>
 hipError_t launch_kind(const PartialArgs &a, hipStream_t stream)
 {
     const int M = a.rows_per_kv;
     if (persistent_shape(a)) {
         const bool fa = a.new_k != nullptr && a.n_new > 0;
         if (a.batch <= 64)
-            return fa ? launch_persistent<D, KVT, PVS, 1, true>(a, stream)
-                      : launch_persistent<D, KVT, PVS, 1, false>(a, stream);
-        return fa ? launch_persistent<D, KVT, PVS, 4, true>(a, stream)
-                  : launch_persistent<D, KVT, PVS, 4, false>(a, stream);
+            return fa ? launch_persistent<D, DV, KVT, PVS, 1, true>(a, stream)
+                      : launch_persistent<D, DV, KVT, PVS, 1, false>(a, stream);
+        return fa ? launch_persistent<D, DV, KVT, PVS, 4, true>(a, stream)
+                  : launch_persistent<D, DV, KVT, PVS, 4, false>(a, stream);
     }
     if (a.new_k != nullptr && a.n_new > 0)
         return hipErrorInvalidValue;           // the caller appends first for these shapes
@@ -1169,11 +1180,14 @@ hipError_t launch_kind(const PartialArgs &a, hipStream_t stream)
             return hipErrorInvalidConfiguration;
         dim3 grid((unsigned)blocks);
         if (chunks >= 16)
-            hipLaunchKernelGGL((decode_mfma_kernel<D, KVT, PVS, 4>), grid, dim3(256), 0, stream, a);
+            hipLaunchKernelGGL((decode_mfma_kernel<D, DV, KVT, PVS, 4>), grid, dim3(256), 0, stream,
+                               a);
         else if (chunks >= 4)
-            hipLaunchKernelGGL((decode_mfma_kernel<D, KVT, PVS, 2>), grid, dim3(128), 0, stream, a);
+            hipLaunchKernelGGL((decode_mfma_kernel<D, DV, KVT, PVS, 2>), grid, dim3(128), 0, stream,
+                               a);
         else
-            hipLaunchKernelGGL((decode_mfma_kernel<D, KVT, PVS, 1>), grid, dim3(64), 0, stream, a);
+            hipLaunchKernelGGL((decode_mfma_kernel<D, DV, KVT, PVS, 1>), grid, dim3(64), 0, stream,
+                               a);
         return hipGetLastError();
     }
     const int64_t heads = (int64_t)a.batch * a.kv_heads * a.n_split;
@@ -1185,10 +1199,10 @@ hipError_t launch_kind(const PartialArgs &a, hipStream_t stream)
     if (blocks > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
     if (nt == 2)
-        hipLaunchKernelGGL((multirow_mfma_kernel<D, KVT, PVS, 2, kMrNK, kMrNSet>),
+        hipLaunchKernelGGL((multirow_mfma_kernel<D, DV, KVT, PVS, 2, kMrNK, kMrNSet>),
                            dim3((unsigned)blocks), dim3(512), 0, stream, a, row_blocks);
     else
-        hipLaunchKernelGGL((multirow_mfma_kernel<D, KVT, PVS, 1, kMrNK, kMrNSet>),
+        hipLaunchKernelGGL((multirow_mfma_kernel<D, DV, KVT, PVS, 1, kMrNK, kMrNSet>),
                            dim3((unsigned)blocks), dim3(512), 0, stream, a, row_blocks);
     return hipGetLastError();
 }
@@ -1197,9 +1211,10 @@ template <int KVT, bool PVS>
 hipError_t launch_d(const PartialArgs &a, hipStream_t stream)
 {
     switch (a.head_dim) {
-    case 64: return launch_kind<64, KVT, PVS>(a, stream);
-    case 128: return launch_kind<128, KVT, PVS>(a, stream);
-    default: return launch_kind<256, KVT, PVS>(a, stream);
+    case 64: return launch_kind<64, 64, KVT, PVS>(a, stream);
+    case 128: return launch_kind<128, 128, KVT, PVS>(a, stream);
+    case 192: return launch_kind<192, 128, KVT, PVS>(a, stream);   // the only pair with 192
+    default: return launch_kind<256, 256, KVT, PVS>(a, stream);
     }
 }
 

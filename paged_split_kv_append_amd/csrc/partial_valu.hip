@@ -14,8 +14,9 @@
 //   A. 4 threads per position form q . k for every row (D/4 elements each,
 //      combined by lane shuffles) and write the scaled score to LDS;
 //   B. one wave per row takes the chunk max, rescales, forms p = 2^(s - m);
-//   C. each thread owns one element e of the head dim and a position phase,
-//      accumulating p * v[e]; phases are summed in a fixed order at the end.
+//   C. each thread owns one element e of the V head dim DV (which may differ
+//      from the q/k head dim D) and a position phase, accumulating p * v[e];
+//      phases are summed in a fixed order at the end.
 // Scores are kept in log2 units (scale * log2 e folded in); m is stored back
 // in natural-log units.
 #include "device_common.h"
@@ -37,17 +38,17 @@ __device__ __forceinline__ float load_q(const void *q, int64_t i)
         return bf16_bits_to_f32(((const uint16_t *)q)[i]);
 }
 
-template <int KVT, int QT, int D, int RB>
+template <int KVT, int QT, int D, int DV, int RB>
 __global__ void __launch_bounds__(kThreads)
 partial_valu_kernel(PartialArgs a)
 {
-    constexpr int PG = kThreads / D;          // position phases in step C
+    constexpr int PG = kThreads / DV;         // position phases in step C
     __shared__ float q_s[RB][D];
     __shared__ float p_s[RB][kChunk];
     __shared__ int32_t page_s[kChunk];
     __shared__ float m_s[RB], l_s[RB], corr_s[RB];
     __shared__ int32_t n_s[RB];
-    __shared__ float red_s[PG][RB][D];
+    __shared__ float red_s[PG][RB][DV];
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int rb = blockIdx.x, s = blockIdx.y;
@@ -88,7 +89,7 @@ partial_valu_kernel(PartialArgs a)
     const int j_end = min(j_begin + S, n_max);
     const float scale2 = a.scale * a.k_scale * kLog2e;
 
-    const int e_c = t % D, pg = t / D;
+    const int e_c = t % DV, pg = t / DV;
     float acc[RB];
 #pragma unroll
     for (int i = 0; i < RB; ++i)
@@ -183,14 +184,14 @@ partial_valu_kernel(PartialArgs a)
     for (int i = 0; i < RB; ++i)
         red_s[pg][i][e_c] = acc[i];
     __syncthreads();
-    for (int idx = t; idx < rows_here * D; idx += kThreads) {
-        const int i = idx / D, e = idx % D;
+    for (int idx = t; idx < rows_here * DV; idx += kThreads) {
+        const int i = idx / DV, e = idx % DV;
         float o = 0.0f;
 #pragma unroll
         for (int k = 0; k < PG; ++k)
             o += red_s[k][i][e];
         const int64_t row = row_base + row0 + i;
-        a.o_part[(row * a.n_split + s) * D + e] = o;
+        a.o_part[(row * a.n_split + s) * DV + e] = o;
         if (e == 0) {
             const float m = m_s[i];
             a.m_part[row * a.n_split + s] = m == -INFINITY ? -INFINITY : m * kLn2;
@@ -199,7 +200,7 @@ partial_valu_kernel(PartialArgs a)
     }
 }
 
-template <int KVT, int QT, int D>
+template <int KVT, int QT, int D, int DV>
 hipError_t launch_rb(const PartialArgs &a, hipStream_t stream)
 {
     const int M = a.rows_per_kv;
@@ -207,7 +208,7 @@ hipError_t launch_rb(const PartialArgs &a, hipStream_t stream)
 #define NBX_LAUNCH(RB_)                                                                   \
     do {                                                                                  \
         grid.x = (M + (RB_)-1) / (RB_);                                                   \
-        hipLaunchKernelGGL((partial_valu_kernel<KVT, QT, D, RB_>), grid, dim3(kThreads), \
+        hipLaunchKernelGGL((partial_valu_kernel<KVT, QT, D, DV, RB_>), grid, dim3(kThreads), \
                            0, stream, a);                                                 \
     } while (0)
     if (M <= 1)
@@ -226,9 +227,10 @@ template <int KVT, int QT>
 hipError_t launch_d(const PartialArgs &a, hipStream_t stream)
 {
     switch (a.head_dim) {
-    case 64: return launch_rb<KVT, QT, 64>(a, stream);
-    case 128: return launch_rb<KVT, QT, 128>(a, stream);
-    default: return launch_rb<KVT, QT, 256>(a, stream);
+    case 64: return launch_rb<KVT, QT, 64, 64>(a, stream);
+    case 128: return launch_rb<KVT, QT, 128, 128>(a, stream);
+    case 192: return launch_rb<KVT, QT, 192, 128>(a, stream);   // the only pair with 192
+    default: return launch_rb<KVT, QT, 256, 256>(a, stream);
     }
 }
 

@@ -37,7 +37,11 @@ class DevCase:
 
     def append(self):
         kp, vp = self.pools()
-        nb.nbx_paged_kv_append(self.new_k, self.new_v, kp, vp, self.slots, dev_err=self.err)
+        if self.k.shape[3] == self.v.shape[3]:
+            nb.nbx_paged_kv_append(self.new_k, self.new_v, kp, vp, self.slots, dev_err=self.err)
+        else:                                  # pools of different head dims: one call each
+            nb.nbx_paged_kv_append(self.new_k, None, kp, None, self.slots, dev_err=self.err)
+            nb.nbx_paged_kv_append(self.new_v, None, vp, None, self.slots, dev_err=self.err)
 
     def decode(self, n_split=None, split_size=None, out_dtype=torch.float32):
         if n_split is None:
@@ -45,18 +49,18 @@ class DevCase:
         c = self.case
         kp, vp = self.pools()
         rows = c.rows
-        ws = torch.empty(nb.nbx_paged_decode_workspace_bytes(rows, n_split, c.head_dim),
+        ws = torch.empty(nb.nbx_paged_decode_workspace_bytes(rows, n_split, c.v_head_dim),
                          dtype=torch.uint8, device=self.q.device)
-        out = torch.empty(c.batch, c.q_heads, c.q_rows, c.head_dim, dtype=out_dtype,
+        out = torch.empty(c.batch, c.q_heads, c.q_rows, c.v_head_dim, dtype=out_dtype,
                           device=self.q.device)
         nb.nbx_paged_decode(self.q, kp, vp, self.bt, self.lens, c.softmax_scale, split_size,
                             n_split, ws, out, causal=c.causal, dev_err=self.err)
-        return out.reshape(rows, c.head_dim)
+        return out.reshape(rows, c.v_head_dim)
 
     def step(self, new_k=None, new_v=None, n_split=None, split_size=None,
              out_dtype=torch.float32):
-        """nbx_paged_decode_step; new_k / new_v [batch, n_new, kv_heads, D] (default: the
-        case's own new tokens, one per sequence)."""
+        """nbx_paged_decode_step; new_k / new_v [batch, n_new, kv_heads, D / Dv] (default:
+        the case's own new tokens, one per sequence)."""
         if n_split is None:
             n_split, split_size = self.plan()
         c = self.case
@@ -64,13 +68,14 @@ class DevCase:
             new_k, new_v = self.new_k.unsqueeze(1), self.new_v.unsqueeze(1)
         kp, vp = self.pools()
         dev = self.q.device
-        ws = torch.empty(nb.nbx_paged_decode_workspace_bytes(c.rows, n_split, c.head_dim),
+        ws = torch.empty(nb.nbx_paged_decode_workspace_bytes(c.rows, n_split, c.v_head_dim),
                          dtype=torch.uint8, device=dev)
-        out = torch.empty(c.batch, c.q_heads, c.q_rows, c.head_dim, dtype=out_dtype, device=dev)
+        out = torch.empty(c.batch, c.q_heads, c.q_rows, c.v_head_dim, dtype=out_dtype,
+                          device=dev)
         nb.nbx_paged_decode_step(self.q, kp, vp, self.bt, self.lens, c.softmax_scale, split_size,
                                  n_split, ws, out, new_k=new_k, new_v=new_v, causal=c.causal,
                                  dev_err=self.err)
-        return out.reshape(c.rows, c.head_dim)
+        return out.reshape(c.rows, c.v_head_dim)
 
     def partial(self, n_split=None, split_size=None):
         if n_split is None:
@@ -78,7 +83,7 @@ class DevCase:
         c = self.case
         kp, vp = self.pools()
         dev = self.q.device
-        o = torch.empty(c.rows, n_split, c.head_dim, dtype=torch.float32, device=dev)
+        o = torch.empty(c.rows, n_split, c.v_head_dim, dtype=torch.float32, device=dev)
         m = torch.empty(c.rows, n_split, dtype=torch.float32, device=dev)
         l = torch.empty(c.rows, n_split, dtype=torch.float32, device=dev)
         nb.nbx_paged_decode_partial(self.q, kp, vp, self.bt, self.lens, c.softmax_scale,

@@ -66,6 +66,11 @@ def pool(**kw):
     return nb.nbx_kv_pool(**d)
 
 
+def wide(D):
+    """A contiguous pool of head dim D."""
+    return pool(head_dim=D, stride_token=D, stride_head=16 * D, stride_page=2 * 16 * D)
+
+
 def partial_status(lib, k=None, v=None, q_dtype=1, batch=2, q_heads=4, q_rows=1, causal=0,
                    max_pages=4, split=256, n_split=2, q=FAKE, bt=FAKE, sl=FAKE, o=FAKE, m=FAKE,
                    l=FAKE, scale=0.1):
@@ -94,6 +99,12 @@ def partial_status(lib, k=None, v=None, q_dtype=1, batch=2, q_heads=4, q_rows=1,
     (dict(causal=2), -3), (dict(q_rows=0), -3), (dict(max_pages=0), -3),
     (dict(k=pool(dtype=0), v=pool(dtype=1)), -3),
     (dict(batch=0), 0),
+    # (q/k, v) head dims: equal, or the 192 / 128 pair only
+    (dict(k=wide(192), v=wide(128), batch=0), 0),
+    (dict(k=wide(192), v=wide(192)), -3),
+    (dict(k=wide(128), v=wide(64)), -3),
+    (dict(k=wide(256), v=wide(128)), -3),
+    (dict(k=wide(128), v=wide(192)), -3),
 ])
 def test_partial_validation(lib, kw, status):
     assert partial_status(lib, **kw) == status
@@ -112,6 +123,7 @@ def test_append_validation(lib):
     assert f(st=260) == -4
     assert f(nk=FAKE + 8) == -4
     assert f(vp=pool(num_pages=9)) == -3
+    assert f(kp=wide(192), vp=wide(128), sh=192, st=384) == -3   # one call per pool width
     assert f(n=0) == 0                           # no-op, nothing launched
 
 
@@ -121,6 +133,7 @@ def test_merge_validation(lib):
     assert m(o=None) == -1
     assert m(dt=2) == -2
     assert m(D=100) == -3
+    assert m(D=192) == -3                        # 192 is a q/k width, never a value width
     assert m(ns=0) == -3
     assert m(ns=4097) == -6
     assert m(out=FAKE + 2) == -4

@@ -52,9 +52,9 @@ def _poison_slots(case, slots):
 def _check_step(case, dc, out, new_k, new_v, slots):
     """Output against the oracle after its append of new_k/new_v at `slots`; pools bitwise."""
     n_tok = new_k.shape[0] * new_k.shape[1]
-    H, D = case.kv_heads, case.head_dim
+    H, D, Dv = case.kv_heads, case.head_dim, case.v_head_dim
     nk = new_k.float().cpu().reshape(n_tok, H, D)
-    nv = new_v.float().cpu().reshape(n_tok, H, D)
+    nv = new_v.float().cpu().reshape(n_tok, H, Dv)
     kp, bk = oracle.append(nk, "f32", case.k_pool, case.kv_dtype, case.k_scale, case.page_tokens,
                            slots)
     vp, bv = oracle.append(nv, "f32", case.v_pool, case.kv_dtype, case.v_scale, case.page_tokens,
