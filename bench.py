@@ -310,11 +310,7 @@ def main():
     if has_append:
         new_k, new_v = case.new_k.to(dev), case.new_v.to(dev)
         slots = torch.from_numpy(case.slot_mapping).to(dev)
-    if case.split_policy[0] == "fixed":
-        n_split, split = case.split_policy[2], case.split_policy[1]
-    else:
-        n_split, split = nb.nbx_paged_decode_plan(int(case.seq_lens.max()), case.split_policy[1],
-                                                  case.split_policy[2])
+    n_split, split = nb.case_plan(case)
     rows, D = case.rows, case.v_head_dim          # partial and output columns
     o_part = torch.empty(rows, n_split, D, device=dev)
     m_part = torch.empty(rows, n_split, device=dev)

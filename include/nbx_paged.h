@@ -131,6 +131,27 @@ int nbx_paged_kv_append(const void *new_k, const void *new_v, int32_t new_dtype,
 int nbx_paged_decode_plan(int32_t max_seq_len, int32_t split_positions, int32_t max_splits,
                           int32_t *n_split, int32_t *split_size);
 
+/*
+ * nbx_paged_decode_plan_rows - host only.  A split plan that also looks at the
+ * rows per KV head, rows_per_kv = (q_heads / kv_heads) * q_rows.  At most 16
+ * (decode): nbx_paged_decode_plan(max_seq_len, 256, 64).  More (verify
+ * windows, prompt chunks): each (sequence, KV head, split, block of 128 or
+ * 256 rows) is one workgroup of the multi-row kernel, which holds a compute
+ * unit alone, so
+ *   n_split    = clamp(floor(CUs / (batch * kv_heads * row_blocks)), 1,
+ *                      min(64, ceil(longest / 16)))
+ *   split_size = ceil(ceil(longest / n_split) / 16) * 16
+ * with CUs the current device's compute units: the workgroups fill the
+ * device in one round, and the fewest splits that do so keep the partials
+ * (rows * n_split * (Dv + 2) * 4 bytes, written and read back) small.
+ * Reads the device attribute only.  NBX_ERR_BAD_SHAPE for sizes < 1,
+ * q_heads % kv_heads != 0 or an unsupported head_dim (of q and k);
+ * NBX_ERR_LAUNCH if the device cannot be queried.
+ */
+int nbx_paged_decode_plan_rows(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t q_rows,
+                               int32_t head_dim, int32_t max_seq_len, int32_t *n_split,
+                               int32_t *split_size);
+
 /* nbx_paged_decode_workspace_bytes - host only.  Bytes of workspace that
  * nbx_paged_decode needs for `rows` query rows: the partials o [rows,
  * n_split, head_dim], m and l [rows, n_split], fp32, each 256-byte aligned.

@@ -67,6 +67,9 @@ def load_library():
             lib.nbx_paged_decode_plan.argtypes = [I32, I32, I32, ctypes.POINTER(I32),
                                                   ctypes.POINTER(I32)]
             lib.nbx_paged_decode_plan.restype = ctypes.c_int
+            lib.nbx_paged_decode_plan_rows.argtypes = [I32, I32, I32, I32, I32, I32,
+                                                       ctypes.POINTER(I32), ctypes.POINTER(I32)]
+            lib.nbx_paged_decode_plan_rows.restype = ctypes.c_int
             lib.nbx_paged_decode_workspace_bytes.argtypes = [I64, I32, I32]
             lib.nbx_paged_decode_workspace_bytes.restype = SZ
             lib.nbx_paged_decode_partial.argtypes = [P, I32, I32, I32, I32, I32, PP, PP, P, I32, P,
@@ -160,6 +163,34 @@ def nbx_paged_decode_plan(max_seq_len: int, split_positions: int = 256, max_spli
                                                 int(max_splits), ctypes.byref(n), ctypes.byref(s)),
            "nbx_paged_decode_plan")
     return n.value, s.value
+
+
+def nbx_paged_decode_plan_rows(batch: int, q_heads: int, kv_heads: int, q_rows: int,
+                               head_dim: int, max_seq_len: int):
+    """Returns (n_split, split_size): the pages' rule for decode rows, one round of
+    multi-row workgroups over the device's compute units for more rows per KV head."""
+    n = ctypes.c_int32()
+    s = ctypes.c_int32()
+    _check(load_library().nbx_paged_decode_plan_rows(int(batch), int(q_heads), int(kv_heads),
+                                                     int(q_rows), int(head_dim),
+                                                     int(max_seq_len), ctypes.byref(n),
+                                                     ctypes.byref(s)),
+           "nbx_paged_decode_plan_rows")
+    return n.value, s.value
+
+
+def case_plan(case):
+    """(n_split, split_size) of a synthetic case's split policy: ("fixed", S, n),
+    ("rule", positions, cap) -> nbx_paged_decode_plan, ("rows",) ->
+    nbx_paged_decode_plan_rows."""
+    pol = case.split_policy
+    longest = int(case.seq_lens.max()) if len(case.seq_lens) else 1
+    if pol[0] == "fixed":
+        return pol[2], pol[1]
+    if pol[0] == "rows":
+        return nbx_paged_decode_plan_rows(case.batch, case.q_heads, case.kv_heads, case.q_rows,
+                                          case.head_dim, longest)
+    return nbx_paged_decode_plan(longest, pol[1], pol[2])
 
 
 def nbx_paged_decode_workspace_bytes(rows: int, n_split: int, head_dim: int) -> int:

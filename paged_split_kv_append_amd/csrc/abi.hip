@@ -103,6 +103,42 @@ int nbx_paged_decode_plan(int32_t max_seq_len, int32_t split_positions, int32_t 
     return NBX_OK;
 }
 
+int nbx_paged_decode_plan_rows(int32_t batch, int32_t q_heads, int32_t kv_heads, int32_t q_rows,
+                               int32_t head_dim, int32_t max_seq_len, int32_t *n_split,
+                               int32_t *split_size)
+{
+    if (!n_split || !split_size)
+        return NBX_ERR_NULL_PTR;
+    if (batch < 1 || q_heads < 1 || kv_heads < 1 || q_rows < 1 || q_heads % kv_heads ||
+        !head_dim_ok(head_dim))
+        return NBX_ERR_BAD_SHAPE;
+    const int64_t rows_per_kv = (int64_t)(q_heads / kv_heads) * q_rows;
+    if (rows_per_kv <= 16)
+        return nbx_paged_decode_plan(max_seq_len, 256, 64, n_split, split_size);
+    if (rows_per_kv > INT32_MAX)
+        return NBX_ERR_BAD_SHAPE;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+        return NBX_ERR_LAUNCH;
+    const int64_t units = (int64_t)batch * kv_heads *
+                          nbx::multirow_row_blocks((int)rows_per_kv, head_dim);
+    const int64_t longest = max_seq_len < 1 ? 1 : max_seq_len;
+    int64_t n = cus / units;                   // workgroups within one round of the CUs
+    const int64_t tiles = (longest + 15) / 16;
+    if (n > 64)
+        n = 64;
+    if (n > tiles)
+        n = tiles;
+    if (n < 1)
+        n = 1;
+    const int64_t per = (longest + n - 1) / n;
+    *n_split = (int32_t)n;
+    *split_size = (int32_t)((per + 15) / 16 * 16);
+    return NBX_OK;
+}
+
 size_t nbx_paged_decode_workspace_bytes(int64_t rows, int32_t n_split, int32_t head_dim)
 {
     if (rows <= 0 || n_split <= 0 || head_dim <= 0)

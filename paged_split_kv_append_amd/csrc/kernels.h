@@ -123,6 +123,10 @@ hipError_t launch_partial_mfma(const PartialArgs &a, hipStream_t stream);
 // true when launch_partial_mfma runs `a` as one persistent launch, so that it
 // can also perform the append of a.new_k / a.new_v
 bool partial_mfma_is_persistent(const PartialArgs &a);
+// row tiles of 16 per wave, and workgroups per (sequence, KV head, split), of
+// the multi-row kernel for a KV head serving rows_per_kv rows
+int multirow_tiles(int rows_per_kv, int head_dim);
+int multirow_row_blocks(int rows_per_kv, int head_dim);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t stream);
 
 }  // namespace nbx

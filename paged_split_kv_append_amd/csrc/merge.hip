@@ -6,12 +6,15 @@
 // empty one, whose o is not read), w_s = exp(m_s - M), out = sum_s w_s o_s /
 // sum_s w_s l_s.
 //
-// One workgroup of 4 waves per row.  The lanes first take the splits 64 at a
-// time to form M, the weights w_s (kept in LDS) and the denominator by a
-// butterfly sum; then wave k accumulates w_s o_s over the splits s = k, k + 4,
-// ... in ascending order, with 8 independent loads in flight, each lane owning
-// D/64 consecutive elements; the four wave sums are added in order 0..3.  The
-// order is fixed, so repeated runs give identical bits.
+// One workgroup of 4 waves per row, wave k owning the columns [k D/4, (k+1)
+// D/4).  A lane takes 4 consecutive columns of one split, so a wave covers
+// 256 / (D/4) splits per pass; with up to 64 splits every load of the row
+// (m, l and all o pieces) is issued at once and the row takes one memory
+// round trip.  Each lane sums its splits in ascending order, then the lanes
+// holding different splits of the same columns are added by a fixed butterfly
+// (and the denominator by a wave butterfly), so the order is fixed and
+// repeated runs give identical bits.  No LDS and no barrier: the four waves
+// of a row compute M and the denominator alike and are otherwise independent.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -21,91 +24,115 @@ namespace {
 
 constexpr int kMaxSplitsMerge = 4096;
 
+__device__ __forceinline__ float4 fma4(float w, float4 v, float4 acc)
+{
+    return make_float4(fmaf(w, v.x, acc.x), fmaf(w, v.y, acc.y), fmaf(w, v.z, acc.z),
+                       fmaf(w, v.w, acc.w));
+}
+
 template <int D, int OUT>
 __global__ void __launch_bounds__(256)
 merge_kernel(MergeArgs a)
 {
-    constexpr int E = D / 64;
-    __shared__ float w_s[kMaxSplitsMerge];
-    __shared__ float red[4][D];
-    __shared__ float stat[2];                  // M, den
+    constexpr int CW = D / 4;                  // columns per wave
+    constexpr int LPS = CW / 4;                // lanes per split (4 columns each)
+    constexpr int SPP = 64 / LPS;              // splits per pass
+    constexpr int NP = LPS;                    // passes in flight: SPP * NP = 64 splits
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int64_t row = blockIdx.x;
     const int ns = a.n_split;
     const float *m = a.m_part + row * ns;
     const float *l = a.l_part + row * ns;
+    const int sub = lane / LPS;                // this lane's split within a pass
+    const int col = wv * CW + (lane % LPS) * 4;
+    const float *o = a.o_part + row * (int64_t)ns * D + col;
+    const bool den_lane = lane % LPS == 0;     // one lane per split adds w_s l_s
 
-    if (wv == 0) {
-        float M = -INFINITY;
-        bool has_nan = false;
+    float M = -INFINITY;
+    bool has_nan = false;
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float den = 0.0f;
+    auto weight = [&](float ms) {
+        return (ms == -INFINITY || M == -INFINITY) ? 0.0f : exp2f((ms - M) * kLog2e);
+    };
+    if (ns <= SPP * NP) {
+        // one round trip: every piece of the row in flight together
+        float4 v[NP];
+        float ms[NP], ls[NP];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int s = p * SPP + sub;
+            const bool in = s < ns;
+            v[p] = in ? *(const float4 *)(o + (int64_t)s * D) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            ms[p] = in ? m[s] : -INFINITY;
+            ls[p] = in ? l[s] : 0.0f;
+        }
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            has_nan |= ms[p] != ms[p];
+            M = fmaxf(M, ms[p]);
+        }
+        M = wave_max(M);
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const float w = weight(ms[p]);
+            if (w != 0.0f)                     // an empty split's o is not defined: skip it
+                acc = fma4(w, v[p], acc);
+            if (den_lane)
+                den = fmaf(w, ls[p], den);
+        }
+    } else {
         for (int s = lane; s < ns; s += 64) {
             const float ms = m[s];
             has_nan |= ms != ms;
             M = fmaxf(M, ms);
         }
         M = wave_max(M);
-        has_nan = __any(has_nan);
-        float den = 0.0f;
-        for (int s = lane; s < ns; s += 64) {
-            const float ms = m[s];
-            const float w = (ms == -INFINITY || M == -INFINITY) ? 0.0f
-                                                                 : exp2f((ms - M) * kLog2e);
-            w_s[s] = w;
-            den = fmaf(w, l[s], den);
-        }
-        den = wave_sum(den);
-        if (lane == 0) {
-            stat[0] = has_nan ? __builtin_nanf("") : M;
-            stat[1] = den;
-        }
-    }
-    __syncthreads();
-
-    float acc[E];
+        for (int s0 = 0; s0 < ns; s0 += SPP * NP) {
+            float4 v[NP];
+            float ms[NP], ls[NP];
 #pragma unroll
-    for (int k = 0; k < E; ++k)
-        acc[k] = 0.0f;
-    const float *o = a.o_part + row * (int64_t)ns * D + lane * E;
-    int s = wv;
-    for (; s + 28 < ns; s += 32) {             // 8 splits of this wave per batch
-        float v[8][E];
+            for (int p = 0; p < NP; ++p) {
+                const int s = s0 + p * SPP + sub;
+                const bool in = s < ns;
+                v[p] = in ? *(const float4 *)(o + (int64_t)s * D)
+                          : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                ms[p] = in ? m[s] : -INFINITY;
+                ls[p] = in ? l[s] : 0.0f;
+            }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const float *os = o + (int64_t)(s + 4 * u) * D;
-#pragma unroll
-            for (int k = 0; k < E; ++k)
-                v[u][k] = os[k];
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const float w = w_s[s + 4 * u];
-#pragma unroll
-            for (int k = 0; k < E; ++k)   // an empty split's o is not defined: skip it
-                acc[k] = w != 0.0f ? fmaf(w, v[u][k], acc[k]) : acc[k];
+            for (int p = 0; p < NP; ++p) {
+                const float w = weight(ms[p]);
+                if (w != 0.0f)
+                    acc = fma4(w, v[p], acc);
+                if (den_lane)
+                    den = fmaf(w, ls[p], den);
+            }
         }
     }
-    for (; s < ns; s += 4) {
-        const float w = w_s[s];
-        if (w == 0.0f)
-            continue;
-        const float *os = o + (int64_t)s * D;
+    has_nan = __any(has_nan);
+    den = wave_sum(den);
 #pragma unroll
-        for (int k = 0; k < E; ++k)
-            acc[k] = fmaf(w, os[k], acc[k]);
+    for (int off = LPS; off < 64; off <<= 1) {
+        acc.x += __shfl_xor(acc.x, off, 64);
+        acc.y += __shfl_xor(acc.y, off, 64);
+        acc.z += __shfl_xor(acc.z, off, 64);
+        acc.w += __shfl_xor(acc.w, off, 64);
     }
+    if (sub == 0) {
+        float r[4] = {acc.x, acc.y, acc.z, acc.w};
 #pragma unroll
-    for (int k = 0; k < E; ++k)
-        red[wv][lane * E + k] = acc[k];
-    __syncthreads();
-
-    const float M = stat[0], den = stat[1];
-    for (int e = threadIdx.x; e < D; e += 256) {
-        float r = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
-        r = M != M ? __builtin_nanf("") : (den > 0.0f ? r / den : 0.0f);
-        if constexpr (OUT == NBX_F32)
-            ((float *)a.out)[row * D + e] = r;
-        else
-            ((uint16_t *)a.out)[row * D + e] = f32_to_bf16_bits(r);
+        for (int k = 0; k < 4; ++k)
+            r[k] = has_nan ? __builtin_nanf("") : (den > 0.0f ? r[k] / den : 0.0f);
+        if constexpr (OUT == NBX_F32) {
+            *(float4 *)((float *)a.out + row * D + col) = make_float4(r[0], r[1], r[2], r[3]);
+        } else {
+            const uint32_t lo = (uint32_t)f32_to_bf16_bits(r[0]) |
+                                ((uint32_t)f32_to_bf16_bits(r[1]) << 16);
+            const uint32_t hi = (uint32_t)f32_to_bf16_bits(r[2]) |
+                                ((uint32_t)f32_to_bf16_bits(r[3]) << 16);
+            *(uint2 *)((uint16_t *)a.out + row * D + col) = make_uint2(lo, hi);
+        }
     }
 }
 

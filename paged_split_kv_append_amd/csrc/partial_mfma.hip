@@ -1191,10 +1191,8 @@ hipError_t launch_kind(const PartialArgs &a, hipStream_t stream)
         return hipGetLastError();
     }
     const int64_t heads = (int64_t)a.batch * a.kv_heads * a.n_split;
-    // 8 waves x 16 rows per workgroup (8 x 32 where a KV head has more rows
-    // than that and D <= 128: D = 256 would spill at 32 rows per wave)
-    const int nt = M > 128 && D <= 128 ? 2 : 1;
-    const int row_blocks = (M + 128 * nt - 1) / (128 * nt);
+    const int nt = multirow_tiles(M, D);
+    const int row_blocks = multirow_row_blocks(M, D);
     const int64_t blocks = heads * row_blocks;
     if (blocks > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
@@ -1221,6 +1219,19 @@ hipError_t launch_d(const PartialArgs &a, hipStream_t stream)
 }  // namespace
 
 bool partial_mfma_is_persistent(const PartialArgs &a) { return persistent_shape(a); }
+
+// 8 waves x 16 rows per multi-row workgroup (8 x 32 where a KV head has more
+// rows than that and D <= 128: D = 256 would spill at 32 rows per wave)
+int multirow_tiles(int rows_per_kv, int head_dim)
+{
+    return rows_per_kv > 128 && head_dim <= 128 ? 2 : 1;
+}
+
+int multirow_row_blocks(int rows_per_kv, int head_dim)
+{
+    const int r = 128 * multirow_tiles(rows_per_kv, head_dim);
+    return (rows_per_kv + r - 1) / r;
+}
 
 hipError_t launch_partial_mfma(const PartialArgs &a, hipStream_t stream)
 {

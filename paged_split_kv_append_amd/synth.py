@@ -53,17 +53,17 @@ WORKLOADS = {
             lens=("uniform", 1, 4096), split=("rule", 256, 64), append=True, k_mult=1.0),
     3: dict(name="verify", batch=4, q_heads=24, kv_heads=4, head_dim=256, kv_dtype=BF16,
             q_dtype=BF16, page_tokens=16, q_rows=16, causal=True,
-            lens=("fixed", 32768), split=("rule", 256, 64), append=False, k_mult=1.0),
+            lens=("fixed", 32768), split=("rows",), append=False, k_mult=1.0),
     4: dict(name="chunk", batch=1, q_heads=24, kv_heads=4, head_dim=256, kv_dtype=FP8,
             q_dtype=BF16, page_tokens=16, q_rows=128, causal=True,
-            lens=("fixed", 32768), split=("rule", 2048, 16), append=False, k_mult=1.0),
+            lens=("fixed", 32768), split=("rows",), append=False, k_mult=1.0),
     5: dict(name="long", batch=8, q_heads=64, kv_heads=8, head_dim=128, kv_dtype=BF16,
             q_dtype=BF16, page_tokens=32, q_rows=1, causal=False,
             lens=("loguniform", 1024, 131072), split=("rule", 256, 64), append=True,
             k_mult=4.0),
     6: dict(name="windows", batch=4, q_heads=24, kv_heads=4, head_dim=256, kv_dtype=BF16,
             q_dtype=BF16, page_tokens=16, q_rows=16, causal=True,
-            lens=("fixed", 32768), split=("rule", 256, 64), append=False, k_mult=1.0,
+            lens=("fixed", 32768), split=("rows",), append=False, k_mult=1.0,
             windows=(16, 12, 8, 4)),
     7: dict(name="mla", batch=32, q_heads=16, kv_heads=16, head_dim=192, v_head_dim=128,
             kv_dtype=BF16, q_dtype=BF16, page_tokens=16, q_rows=1, causal=False,
@@ -97,7 +97,7 @@ class PagedCase:
     k_scale: float                  # fp32 dequant factor (1.0 unless fp8)
     v_scale: float
     softmax_scale: float            # an fp32 value: 1/sqrt(D) rounded to fp32
-    split_policy: tuple             # ("fixed", S, n) or ("rule", positions, cap)
+    split_policy: tuple             # ("fixed", S, n), ("rule", positions, cap) or ("rows",)
     new_k: Optional[torch.Tensor] = None     # [N_tok, H_kv, D] fp32
     new_v: Optional[torch.Tensor] = None     # [N_tok, H_kv, Dv] fp32
     slot_mapping: Optional[np.ndarray] = None  # [N_tok] int32
@@ -224,10 +224,7 @@ def make_case(workload: int, seed: Optional[int] = None, poison: bool = True,
             k_pool[ip, :, it, :] = nb
             v_pool[ip, :, it, :] = nb
 
-    if cfg["split"][0] == "fixed":
-        split_policy = ("fixed", cfg["split"][1], cfg["split"][2])
-    else:
-        split_policy = ("rule", cfg["split"][1], cfg["split"][2])
+    split_policy = tuple(cfg["split"])
 
     return PagedCase(
         name=cfg["name"], batch=B, q_heads=Hq, kv_heads=Hkv, head_dim=D, q_rows=W,

@@ -29,11 +29,7 @@ class DevCase:
         return nb.KVPool(self.k, self.case.k_scale), nb.KVPool(self.v, self.case.v_scale)
 
     def plan(self):
-        pol = self.case.split_policy
-        if pol[0] == "fixed":
-            return pol[2], pol[1]
-        n, s = nb.nbx_paged_decode_plan(int(self.case.seq_lens.max()), pol[1], pol[2])
-        return n, s
+        return nb.case_plan(self.case)
 
     def append(self):
         kp, vp = self.pools()

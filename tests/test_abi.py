@@ -20,7 +20,8 @@ def test_every_declared_symbol_is_exported(lib):
     assert {"nbx_paged_kv_append", "nbx_paged_decode_partial", "nbx_paged_decode_merge",
             "nbx_paged_decode", "nbx_paged_decode_plan", "nbx_paged_decode_workspace_bytes",
             "nbx_status_str", "nbx_version", "nbx_paged_decode_step",
-            "nbx_paged_lens_advance", "nbx_paged_decode_partial_windows"} <= set(names)
+            "nbx_paged_lens_advance", "nbx_paged_decode_partial_windows",
+            "nbx_paged_decode_plan_rows"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -36,6 +37,28 @@ def test_split_plan_matches_oracle_bit_exact():
     for L in list(range(0, 5000, 7)) + [16383, 16384, 16385, 32768, 100000, 131072, 2 ** 31 - 1]:
         for pos, cap in ((256, 64), (2048, 16), (16, 1024)):
             assert nb.nbx_paged_decode_plan(L, pos, cap) == oracle.split_plan(max(L, 1), pos, cap)
+
+
+def test_rows_plan_is_the_pages_rule_for_decode_rows():
+    for L in (1, 100, 4096, 131072):
+        for hq, hkv, w in ((32, 8, 1), (64, 8, 1), (24, 4, 2), (16, 16, 16)):
+            assert nb.nbx_paged_decode_plan_rows(32, hq, hkv, w, 128, L) == \
+                nb.nbx_paged_decode_plan(L, 256, 64)
+
+
+def test_rows_plan_validation(lib):
+    n, s = ctypes.c_int32(), ctypes.c_int32()
+    f = lambda *a: lib.nbx_paged_decode_plan_rows(*a, ctypes.byref(n), ctypes.byref(s))
+    assert f(0, 24, 4, 16, 256, 100) == -3
+    assert f(4, 24, 5, 16, 256, 100) == -3
+    assert f(4, 24, 4, 16, 96, 100) == -3
+    assert lib.nbx_paged_decode_plan_rows(4, 24, 4, 16, 256, 100, None, ctypes.byref(s)) == -1
+    # more than 16 rows per KV head asks the device for its compute units: without
+    # a device the call reports it, with one the plan covers the sequence
+    st = f(4, 24, 4, 16, 256, 32768)
+    assert st in (0, -7)
+    if st == 0:
+        assert 1 <= n.value <= 64 and s.value % 16 == 0 and n.value * s.value >= 32768
 
 
 def test_plan_rejects_bad_arguments(lib):

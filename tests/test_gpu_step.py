@@ -251,6 +251,18 @@ def test_device_derived_split_equals_host_plan(workload):
     assert torch.equal(o1[keep], o2[keep])
 
 
+def test_rows_plan_fills_one_round_of_compute_units():
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for B, hq, hkv, W, D, L in ((4, 24, 4, 16, 256, 32768), (1, 24, 4, 128, 256, 32768),
+                                (2, 8, 2, 48, 128, 700), (64, 24, 4, 16, 256, 5000)):
+        n, S = nb.nbx_paged_decode_plan_rows(B, hq, hkv, W, D, L)
+        rows = hq // hkv * W
+        per_block = 256 if rows > 128 and D <= 128 else 128
+        units = B * hkv * -(-rows // per_block)
+        assert n == max(1, min(cus // units, 64, -(-L // 16))), (B, hq, hkv, W, D, L, n)
+        assert S == (-(-L // n) + 15) // 16 * 16
+
+
 def test_lens_advance():
     lens = torch.tensor([0, 5, 100, 7], dtype=torch.int32, device="cuda")
     nb.nbx_paged_lens_advance(lens, 3)
