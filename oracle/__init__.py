@@ -61,6 +61,10 @@ def _load():
             lib.oracle_partials.argtypes = common + [I64, I, P, P, P]
             lib.oracle_partials.restype = I
             lib.oracle_merge.argtypes = [P, P, P, I64, I, I, P]
+            lib.oracle_fixed_shift_constants.argtypes = [I64, D, P, P, P]
+            lib.oracle_fixed_shift_constants.restype = I
+            lib.oracle_kv_bounds.argtypes = [P, I, I64, I, I, I, I, P, I, P, I, P]
+            lib.oracle_kv_bounds.restype = I
             lib.oracle_set_mutation.argtypes = [I]
             lib.oracle_get_mutation.restype = I
             lib.oracle_num_threads.restype = I
@@ -203,6 +207,31 @@ def merge(o, m, l) -> np.ndarray:
     rows, n_split, D = o.shape
     out = np.zeros((rows, D))
     _load().oracle_merge(_ptr(o), _ptr(m), _ptr(l), rows, n_split, D, _ptr(out))
+    return out
+
+
+def fixed_shift_constants(n: int, v_max: float = 256.0):
+    """(C, W, gate) of the fixed-shift softmax for N = n keys and values bounded by v_max."""
+    c, w, g = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    st = _load().oracle_fixed_shift_constants(int(n), float(v_max), ctypes.byref(c),
+                                              ctypes.byref(w), ctypes.byref(g))
+    if st != 0:
+        raise ValueError("oracle: n >= 1 and finite v_max >= 1 required")
+    return int(c.value), int(w.value), int(g.value)
+
+
+def kv_bounds(pool, dtype: str, block_table, seq_lens, is_value: bool) -> np.ndarray:
+    """Per (page, KV head) bound over the rows the sequences hold: largest K row norm
+    (is_value False) or largest |V element| (True), stored units -> [P, H_kv] float64."""
+    pl = _np(pool)
+    P, Hkv, T, D = pl.shape
+    bt = np.ascontiguousarray(np.asarray(block_table, dtype=np.int32))
+    sl = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    out = np.zeros((P, Hkv))
+    st = _load().oracle_kv_bounds(_ptr(pl), _CODES[dtype], P, Hkv, T, D, int(bool(is_value)),
+                                  _ptr(bt), bt.shape[1], _ptr(sl), len(sl), _ptr(out))
+    if st != 0:
+        raise ValueError("oracle: a held position has no page in the pool")
     return out
 
 

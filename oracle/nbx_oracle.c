@@ -41,6 +41,14 @@
  *  - oracle_split_plan: splits = max(1, min(ceil(longest/256), 64)) and the
  *    split length ceil(ceil(longest/splits)/A)*A (paged_decode_attn.py,
  *    paged_decode_splits and the kernel's seg_len).
+ *  - oracle_fixed_shift_constants: the fixed-shift softmax constants of the
+ *    maxdiffusion PR #477 page (dynamic bounds): C(N) = 127 - ceil(log2 N) -
+ *    ceil(log2 Vmax), W(N) = C(N) + 125, gate = floor(W/2).
+ *  - oracle_kv_bounds: the quantities those bounds are built from, per page
+ *    and KV head: the largest Euclidean norm of a stored K row and the largest
+ *    |element| of a stored V row over the positions the sequences hold
+ *    (maxdiffusion PR #477: U_B is a product of the largest query norm and the
+ *    largest key norm; the V magnitude bound enters C(N)).
  *
  * All arithmetic on values is in double.  Products of two stored values and a
  * scale are exact in double; sums round at 2^-53.
@@ -539,6 +547,74 @@ void oracle_merge(const double *o, const double *m, const double *l, int64_t row
         for (int e = 0; e < D; ++e)
             dst[e] = den > 0.0 ? dst[e] / den : 0.0;
     }
+}
+
+/* ------------------------------------------------------------------ fixed shift */
+
+/* smallest integer k with 2^k >= x, for x >= 1 (exact: frexp) */
+static int64_t ceil_log2(double x)
+{
+    int e;
+    double f = frexp(x, &e);          /* x = f * 2^e, f in [0.5, 1) */
+    return f == 0.5 ? e - 1 : e;
+}
+
+/* C(N) = 127 - ceil(log2 N) - ceil(log2 v_max), W = C + 125, gate = floor(W / 2).
+ * n >= 1 and v_max >= 1, else -1. */
+int oracle_fixed_shift_constants(int64_t n, double v_max, int64_t *c, int64_t *w, int64_t *gate)
+{
+    int64_t cc, ww;
+    if (n < 1 || !(v_max >= 1.0) || isinf(v_max))
+        return -1;
+    cc = 127 - ceil_log2((double)n) - ceil_log2(v_max);
+    ww = cc + 125;
+    *c = cc;
+    *w = ww;
+    *gate = ww >= 0 ? ww / 2 : -((-ww + 1) / 2);     /* floor division */
+    return 0;
+}
+
+/* bounds[page * Hkv + h]: over the rows (page, h, row) holding a position
+ * j < L_b of some sequence b (page = block_table[b, j / T], row = j mod T),
+ * the largest Euclidean norm of the stored row (is_value == 0) or the largest
+ * |stored element| (is_value != 0), in stored units (pool scale not applied).
+ * A NaN element makes its bound NaN; rows no sequence holds leave 0.
+ * Returns -1 if a held position has no page in the pool. */
+int oracle_kv_bounds(const void *pool, int dtype, int64_t P, int Hkv, int T, int D, int is_value,
+                     const int32_t *block_table, int max_pages, const int32_t *seq_lens, int B,
+                     double *bounds)
+{
+    for (int64_t i = 0; i < P * Hkv; ++i)
+        bounds[i] = 0.0;
+    for (int b = 0; b < B; ++b) {
+        int64_t L = seq_lens[b];
+        for (int64_t j = 0; j < L; ++j) {
+            int64_t page = block_table[(int64_t)b * max_pages + j / T];
+            if (page < 0 || page >= P)
+                return -1;
+            for (int h = 0; h < Hkv; ++h) {
+                int64_t base = ((page * Hkv + h) * T + j % T) * (int64_t)D;
+                double v = 0.0, *dst = &bounds[page * Hkv + h];
+                int nan = 0;
+                for (int e = 0; e < D; ++e) {
+                    double x = oracle_decode_value(dtype, pool, base + e);
+                    if (isnan(x))
+                        nan = 1;
+                    else if (is_value)
+                        v = fabs(x) > v ? fabs(x) : v;
+                    else
+                        v += x * x;
+                }
+                if (!is_value)
+                    v = sqrt(v);
+                if (nan || isnan(*dst))
+                    *dst = NAN;
+                else if (v > *dst)
+                    *dst = v;
+            }
+        }
+    }
+    return 0;
 }
 
 size_t oracle_elem_size(int dtype) { return elem_size(dtype); }

@@ -290,6 +290,86 @@ def test_value_head_dim_matches_torch_sdpa_float64(seed, W, causal, Hq, Hkv, D, 
     assert np.allclose(out, sdpa_reference(p, scale), atol=1e-12, rtol=0)
 
 
+# ----------------------------------------------------------------- fixed-shift bounds
+
+def test_fixed_shift_constants_match_the_page_examples():
+    g = json.load(open(os.path.join(GOLDEN, "fixed_shift_constants.json")))
+    for ex in g["examples"]:
+        assert oracle.fixed_shift_constants(ex["N"], g["v_max_bound"]) == \
+            (ex["C"], ex["W"], ex["gate"]), ex["where"]
+    adv = g["adversarial"]
+    C, W, gate = oracle.fixed_shift_constants(adv["N"], g["v_max_bound"])
+    U = math.hypot(*adv["q"]) * adv["max_key_norm"]
+    assert (math.ceil(U) <= W) == adv["passes_a_W_sized_gate"]
+    assert (math.ceil(U) <= gate) == adv["passes_the_shipped_gate"]
+
+
+@pytest.mark.parametrize("n,vmax,c", [(1, 1.0, 127), (2, 1.0, 126), (4096, 256.0, 107),
+                                      (4097, 256.0, 106), (4096, 257.0, 106),
+                                      (4096, 255.5, 107), (131072, 448.0, 101)])
+def test_fixed_shift_constants_at_power_of_two_edges(n, vmax, c):
+    C, W, gate = oracle.fixed_shift_constants(n, vmax)
+    assert C == c and W == c + 125 and gate == (c + 125) // 2
+
+
+def test_fixed_shift_gate_keeps_every_term_normal_and_every_sum_finite():
+    # the page's argument: for |z| <= U and m = ceil(U) - C, every z - m lies in
+    # [-125, C] once ceil(U) <= gate, so 2^(z - m) is a normal fp32 number and N
+    # terms of size <= Vmax sum below 2^127
+    for n, vmax in ((4096, 256.0), (75600, 256.0), (131072, 448.0), (1, 1.0)):
+        C, W, gate = oracle.fixed_shift_constants(n, vmax)
+        for cu in range(0, gate + 1):
+            U = float(cu)                      # worst case U = ceil(U)
+            m = cu - C
+            assert -U - m >= -125 and U - m <= C
+            assert n * 2.0 ** (U - m) * vmax <= 2.0 ** 127
+        # one step past the gate the lowest term can leave the normal range
+        U = float(gate + 1)
+        assert -U - (gate + 1 - C) < -125
+
+
+def test_kv_bounds_closed_forms():
+    # rows c * e_i have norm |c|; the V bound is the largest |element| held
+    T, D, P, H = 16, 32, 4, 2
+    k = np.zeros((P, H, T, D), np.float32)
+    v = np.zeros((P, H, T, D), np.float32)
+    for p_ in range(P):
+        for h in range(H):
+            for r in range(T):
+                k[p_, h, r, (r + h) % D] = (p_ + 1) * (r + 1) * (-1) ** r
+                v[p_, h, r, (3 * r) % D] = -(p_ * 10 + h + r * 0.5)
+    bt = np.array([[2, 0, -1], [3, -1, -1]], np.int32)     # page 1 belongs to nobody
+    lens = np.array([20, 7], np.int32)                     # page 0 holds rows 0-3 only
+    kb = oracle.kv_bounds(k, "f32", bt, lens, is_value=False)
+    vb = oracle.kv_bounds(v, "f32", bt, lens, is_value=True)
+    # held rows: page 2 rows 0-15, page 0 rows 0-3, page 3 rows 0-6
+    for h in range(H):
+        assert kb[2, h] == 3 * 16 and kb[0, h] == 1 * 4 and kb[3, h] == 4 * 7 and kb[1, h] == 0
+        assert vb[2, h] == 20 + h + 7.5 and vb[0, h] == h + 1.5 and vb[3, h] == 30 + h + 3.0
+        assert vb[1, h] == 0
+    v[0, 1, 2, 5] = np.nan                               # held row: NaN sticks
+    v[0, 0, 9, 5] = np.nan                               # unheld row of a held page: ignored
+    vb = oracle.kv_bounds(v, "f32", bt, lens, is_value=True)
+    assert np.isnan(vb[0, 1]) and vb[0, 0] == 1.5
+
+
+def test_kv_bounds_bound_every_logit():
+    # Cauchy-Schwarz: |scale q . k_j| <= scale |q| max_j |k_j| over the held rows
+    c = synth.make_case(2, seed=29, batch=3, lens=("uniform", 1, 300), append=False)
+    kb = oracle.kv_bounds(c.k_pool, c.kv_dtype, c.block_table, c.seq_lens, is_value=False)
+    vb = oracle.kv_bounds(c.v_pool, c.kv_dtype, c.block_table, c.seq_lens, is_value=True)
+    assert np.all(np.isfinite(kb)) and np.all(np.isfinite(vb))
+    k = c.k_pool.float().numpy().astype(np.float64)
+    v = c.v_pool.float().numpy().astype(np.float64)
+    T = c.page_tokens
+    for b in range(c.batch):
+        for j in range(int(c.seq_lens[b])):
+            p_ = c.block_table[b, j // T]
+            for h in range(c.kv_heads):
+                assert np.linalg.norm(k[p_, h, j % T]) <= kb[p_, h] * (1 + 1e-15)
+                assert np.max(np.abs(v[p_, h, j % T])) <= vb[p_, h]
+
+
 # ----------------------------------------------------------------- invariants
 
 def test_page_placement_invariance_is_exact():
