@@ -266,6 +266,9 @@ def main():
     ap.add_argument("--unfused", action="store_true",
                     help="time the append, partial and merge as three calls instead of the "
                          "single-launch step")
+    ap.add_argument("--bounds", action="store_true",
+                    help="attach per-page K/V bounds to the pools (fixed-shift softmax), "
+                         "computed by nbx_paged_kv_bounds before timing")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size "
                          "reference for the profiler's byte counters)")
@@ -307,6 +310,12 @@ def main():
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     kp, vp = nb.KVPool(k, case.k_scale), nb.KVPool(v, case.v_scale)
     has_append = case.new_k is not None
+    if args.bounds:
+        kp.bounds = torch.zeros(k.shape[0], k.shape[1], device=dev)
+        vp.bounds = torch.zeros(k.shape[0], k.shape[1], device=dev)
+        held = case.seq_lens - 1 if has_append else case.seq_lens   # the step appends the rest
+        nb.nbx_paged_kv_bounds(kp, vp, bt, torch.from_numpy(held.astype(np.int32)).to(dev),
+                               dev_err=err)
     if has_append:
         new_k, new_v = case.new_k.to(dev), case.new_v.to(dev)
         slots = torch.from_numpy(case.slot_mapping).to(dev)
@@ -411,7 +420,7 @@ def main():
     # The dominant kernel's bound: HBM unless its matrix-core time at peak
     # exceeds its K/V read time at peak (the 128-row prompt chunk).  fp8 codes
     # are widened to bf16 before the products, so the bf16 MFMA peak applies.
-    traffic = load_traffic(args.workload, fused)
+    traffic = None if args.bounds else load_traffic(args.workload, fused)
     kernel_name = ("split partial with the append fused in" if fused and has_append
                    else "split partial")
     mfma_info = None
@@ -453,6 +462,8 @@ def main():
                             "nbx_paged_kv_append, nbx_paged_decode_partial, "
                             "nbx_paged_decode_merge"),
                    "n_split": n_split, "split_size": split, "rows": rows,
+                   "softmax": ("fixed shift from per-page K/V bounds" if args.bounds
+                               else "running maximum"),
                    "seed": args.seed if args.seed is not None else args.workload},
         "us_per_step": round(float(step_ms.mean()) * 1e3, 2),
         "us_per_step_p10_p90": [round(float(np.percentile(step_ms, 10)) * 1e3, 2),

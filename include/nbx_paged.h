@@ -78,7 +78,31 @@ typedef enum {
 /* A paged K or V pool: data[page * stride_page + head * stride_head +
  * row * stride_token + e] for e in [0, head_dim).  `scale` multiplies every
  * stored element when read (fp8 per-tensor dequantisation factor; 1.0 for
- * fp32 / bf16 pools) and divides a value before it is stored by an append. */
+ * fp32 / bf16 pools) and divides a value before it is stored by an append.
+ *
+ * `bounds` (device fp32 [num_pages, kv_heads], or null) carries, per page and
+ * KV head, an upper bound of what the rows read from it hold, in stored units
+ * (before `scale`): for a K pool the Euclidean norm of a row, for a V pool
+ * the magnitude of an element.  NaN means unknown.  nbx_paged_kv_bounds
+ * computes them from the rows the sequences hold; every append (slot
+ * mapping or decode step) raises them for the rows it writes.  A caller that
+ * writes a pool by other means, or hands a page to another sequence, must
+ * recompute them.  When both pools of a read carry bounds, the split kernels
+ * use the fixed-shift softmax of the maxdiffusion PR #477 page (fixed-m
+ * splash attention, dynamic bounds): each query row i of a split subtracts
+ * the precomputed shift m_i = ceil(U_i) - C(N) instead of a running maximum,
+ * with U_i = |scale * k_scale| * log2(e) * |q_i| * (largest K bound of the
+ * split's pages) (an upper bound of |q_i . k_j| in log2 units, enlarged by
+ * 2^-12 for rounding), C(N) = 127 - ceil(log2 N) - ceil(log2 Vmax),
+ * N = the sequence length, Vmax = max(1, largest V bound of the split's
+ * pages * max(1, v_scale)).  A group of 16 rows uses the shift only if every
+ * row passes the gate ceil(U_i) <= floor((C(N) + 125) / 2); otherwise (and
+ * for NaN or infinite bounds) it keeps the running maximum.  Results agree
+ * with the running-maximum form to rounding; a split's m_part then holds the
+ * shift (natural-log units) instead of the split's largest score, which the
+ * merge handles alike.  Kernels that use it: the single-launch decode kernel
+ * (<= 16 rows per KV head, batch <= 256) and the multi-row kernel; the others
+ * ignore the bounds. */
 typedef struct {
     void *data;             /* device pointer */
     int32_t dtype;          /* nbx_dtype */
@@ -91,6 +115,7 @@ typedef struct {
     int64_t stride_head;
     int64_t stride_token;
     float scale;
+    float *bounds;          /* device [num_pages, kv_heads] or null (see above) */
 } nbx_kv_pool;
 
 /*
@@ -113,12 +138,29 @@ typedef struct {
  * Stored value: same dtype -> bit copy; fp32 -> bf16 round-to-nearest-even
  * (NaN -> 0x7FC0 with the sign kept); bf16 -> fp32 exact; to fp8:
  * round-to-nearest-even of the fp32 quotient value / pool.scale, saturating at
- * +-448, NaN -> 0x7F with the sign kept.  n_tok == 0 is a no-op.
+ * +-448, NaN -> 0x7F with the sign kept.  n_tok == 0 is a no-op.  A pool with
+ * bounds gets bounds[page, head] raised to the stored row's norm (K) or
+ * largest |element| (V).
  */
 int nbx_paged_kv_append(const void *new_k, const void *new_v, int32_t new_dtype, int64_t n_tok,
                         int64_t new_stride_tok, int64_t new_stride_head,
                         const nbx_kv_pool *k_pool, const nbx_kv_pool *v_pool,
                         const int32_t *slot_mapping, int32_t *dev_err, hipStream_t stream);
+
+/*
+ * nbx_paged_kv_bounds - recompute the bounds arrays of both pools (see
+ * nbx_kv_pool) from the rows the sequences hold: bounds[page, h] = the
+ * largest K row norm / |V element| over the rows (page, h, j % page_tokens)
+ * with page = block_table[b, j / page_tokens], j < seq_lens[b]; 0 for pages
+ * no sequence holds.  Both pools need bounds (else NBX_ERR_NULL_PTR) and the
+ * layout rules of a read.  A block-table entry outside the pool sets
+ * NBX_DEVERR_PAGE_RANGE and is skipped; a length outside [0, max_pages *
+ * page_tokens] sets NBX_DEVERR_SEQ_RANGE and is clamped.  Reads every held
+ * K and V element once.
+ */
+int nbx_paged_kv_bounds(const nbx_kv_pool *k_pool, const nbx_kv_pool *v_pool,
+                        const int32_t *block_table, int32_t max_pages, const int32_t *seq_lens,
+                        int32_t batch, int32_t *dev_err, hipStream_t stream);
 
 /*
  * nbx_paged_decode_plan - host only.  The split rule of the nbxtensor

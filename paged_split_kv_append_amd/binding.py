@@ -43,6 +43,7 @@ class nbx_kv_pool(ctypes.Structure):
         ("stride_head", ctypes.c_int64),
         ("stride_token", ctypes.c_int64),
         ("scale", ctypes.c_float),
+        ("bounds", ctypes.c_void_p),
     ]
 
 
@@ -90,6 +91,8 @@ def load_library():
                                                              P, I32, P, F, I32, I32, P, P, P, P,
                                                              P]
             lib.nbx_paged_decode_partial_windows.restype = ctypes.c_int
+            lib.nbx_paged_kv_bounds.argtypes = [PP, PP, P, I32, P, I32, P, P]
+            lib.nbx_paged_kv_bounds.restype = ctypes.c_int
             lib.nbx_status_str.argtypes = [ctypes.c_int]
             lib.nbx_status_str.restype = ctypes.c_char_p
             lib.nbx_version.restype = ctypes.c_int
@@ -137,9 +140,12 @@ class KVPool:
     """A paged pool view [num_pages, kv_heads, page_tokens, head_dim] on the GPU.
 
     ``data`` may be any strided view whose last dim is contiguous; fp8 pools are
-    uint8 (or float8_e4m3fn) tensors of E4M3FN codes with a per-tensor ``scale``."""
+    uint8 (or float8_e4m3fn) tensors of E4M3FN codes with a per-tensor ``scale``.
+    ``bounds``: optional contiguous fp32 [num_pages, kv_heads] tensor of per-page
+    bounds (K row norms / V magnitudes) that turns on the fixed-shift softmax."""
     data: torch.Tensor
     scale: float = 1.0
+    bounds: Optional[torch.Tensor] = None
 
     def desc(self) -> nbx_kv_pool:
         t = self.data
@@ -147,8 +153,14 @@ class KVPool:
             raise ValueError("a pool is a [num_pages, kv_heads, page_tokens, head_dim] view "
                              "with a contiguous last dim")
         P, H, T, D = t.shape
+        bp = None
+        if self.bounds is not None:
+            b = self.bounds
+            if b.dtype != torch.float32 or tuple(b.shape) != (P, H) or not b.is_contiguous():
+                raise ValueError("bounds must be a contiguous fp32 [num_pages, kv_heads] tensor")
+            bp = b.data_ptr()
         return nbx_kv_pool(t.data_ptr(), _dtype_code(t), P, H, T, D, t.stride(0), t.stride(1),
-                           t.stride(2), float(self.scale))
+                           t.stride(2), float(self.scale), bp)
 
 
 def nbx_version() -> int:
@@ -324,6 +336,22 @@ def workspace_partials(workspace, rows: int, n_split: int, head_dim: int):
     off = r256(o_b) + r256(ml_b)
     l = workspace[off:off + ml_b].view(torch.float32).view(rows, n_split)
     return o, m, l
+
+
+def nbx_paged_kv_bounds(k_pool: KVPool, v_pool: KVPool, block_table, seq_lens, dev_err=None,
+                        stream=None):
+    """Recompute k_pool.bounds and v_pool.bounds from the rows the sequences hold."""
+    if k_pool.bounds is None or v_pool.bounds is None:
+        raise ValueError("both pools need a bounds tensor")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous int32 [batch, max_pages] tensor")
+    if seq_lens.dtype != torch.int32 or seq_lens.numel() != block_table.shape[0]:
+        raise ValueError("seq_lens must be int32 [batch]")
+    kd, vd = k_pool.desc(), v_pool.desc()
+    st = load_library().nbx_paged_kv_bounds(ctypes.byref(kd), ctypes.byref(vd), _ptr(block_table),
+                                            block_table.shape[1], _ptr(seq_lens),
+                                            block_table.shape[0], _ptr(dev_err), _stream(stream))
+    _check(st, "nbx_paged_kv_bounds")
 
 
 def nbx_paged_lens_advance(seq_lens, n: int, stream=None):

@@ -47,6 +47,8 @@ int check_pool(const nbx_kv_pool *p)
         return NBX_ERR_BAD_ALIGN;
     if (!(p->scale > 0.0f) || p->scale == INFINITY)
         return NBX_ERR_BAD_SHAPE;
+    if ((uintptr_t)p->bounds & 3u)
+        return NBX_ERR_BAD_ALIGN;
     return NBX_OK;
 }
 
@@ -148,6 +150,51 @@ size_t nbx_paged_decode_workspace_bytes(int64_t rows, int32_t n_split, int32_t h
     return round256(o) + 2 * round256(ml);
 }
 
+int nbx_paged_kv_bounds(const nbx_kv_pool *k_pool, const nbx_kv_pool *v_pool,
+                        const int32_t *block_table, int32_t max_pages, const int32_t *seq_lens,
+                        int32_t batch, int32_t *dev_err, hipStream_t stream)
+{
+    if (!k_pool || !v_pool || !block_table || !seq_lens)
+        return NBX_ERR_NULL_PTR;
+    int st = check_pool(k_pool);
+    if (st != NBX_OK)
+        return st;
+    if ((st = check_pool(v_pool)) != NBX_OK)
+        return st;
+    if (!k_pool->bounds || !v_pool->bounds)
+        return NBX_ERR_NULL_PTR;
+    if (!same_layout(k_pool, v_pool) || !head_dims_ok(k_pool->head_dim, v_pool->head_dim))
+        return NBX_ERR_BAD_SHAPE;
+    if (batch < 0 || max_pages < 1)
+        return NBX_ERR_BAD_SHAPE;
+    if (batch > kMaxGridYZ || max_pages > kMaxGridYZ ||
+        (int64_t)max_pages * k_pool->page_tokens > INT32_MAX)
+        return NBX_ERR_UNSUPPORTED;
+    nbx::BoundsArgs a{};
+    a.k_data = k_pool->data;
+    a.v_data = v_pool->data;
+    a.dtype = k_pool->dtype;
+    a.num_pages = k_pool->num_pages;
+    a.kv_heads = k_pool->kv_heads;
+    a.page_tokens = k_pool->page_tokens;
+    a.head_dim = k_pool->head_dim;
+    a.v_head_dim = v_pool->head_dim;
+    a.k_stride_page = k_pool->stride_page;
+    a.k_stride_head = k_pool->stride_head;
+    a.k_stride_token = k_pool->stride_token;
+    a.v_stride_page = v_pool->stride_page;
+    a.v_stride_head = v_pool->stride_head;
+    a.v_stride_token = v_pool->stride_token;
+    a.k_bounds = k_pool->bounds;
+    a.v_bounds = v_pool->bounds;
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.max_pages = max_pages;
+    a.batch = batch;
+    a.dev_err = dev_err;
+    return to_status(nbx::launch_kv_bounds(a, stream));
+}
+
 int nbx_paged_lens_advance(int32_t *seq_lens, int32_t batch, int32_t n, hipStream_t stream)
 {
     if (!seq_lens)
@@ -209,12 +256,14 @@ int nbx_paged_kv_append(const void *new_k, const void *new_v, int32_t new_dtype,
     a.k_stride_head = k_pool->stride_head;
     a.k_stride_token = k_pool->stride_token;
     a.k_scale = k_pool->scale;
+    a.k_bounds = k_pool->bounds;
     if (v_pool) {
         a.v_data = v_pool->data;
         a.v_stride_page = v_pool->stride_page;
         a.v_stride_head = v_pool->stride_head;
         a.v_stride_token = v_pool->stride_token;
         a.v_scale = v_pool->scale;
+        a.v_bounds = v_pool->bounds;
     }
     a.slot_mapping = slot_mapping;
     a.dev_err = dev_err;
@@ -290,6 +339,8 @@ static nbx::PartialArgs partial_args(const void *q, int32_t q_dtype, int32_t bat
     a.v_stride_token = v_pool->stride_token;
     a.k_scale = k_pool->scale;
     a.v_scale = v_pool->scale;
+    a.k_bounds = k_pool->bounds;
+    a.v_bounds = v_pool->bounds;
     a.block_table = block_table;
     a.max_pages = max_pages;
     a.seq_lens = seq_lens;
@@ -511,6 +562,8 @@ int nbx_paged_decode_step(const void *q, int32_t q_dtype, int32_t batch, int32_t
             ap.v_stride_token = v_pool->stride_token;
             ap.k_scale = k_pool->scale;
             ap.v_scale = v_pool->scale;
+            ap.k_bounds = k_pool->bounds;
+            ap.v_bounds = v_pool->bounds;
             ap.slot_mapping = nullptr;
             ap.dev_err = dev_err;
             ap.seq_lens = seq_lens;

@@ -109,6 +109,46 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
+// ---------------------------------------------------------------- pool bounds
+//
+// Bounds are non-negative floats or NaN ("unknown").  With the sign bit
+// cleared, the bit patterns of non-negative floats order like their values and
+// every NaN lies above +inf, so an unsigned maximum of the patterns keeps a
+// NaN sticky.
+
+__device__ __forceinline__ uint32_t bound_bits(float v) { return __float_as_uint(v) & 0x7FFFFFFFu; }
+
+// raise bounds[i] to v
+__device__ __forceinline__ void raise_bound(float *bounds, int64_t i, float v)
+{
+    atomicMax((unsigned int *)(bounds + i), bound_bits(v));
+}
+
+// NaN-sticky maximum of non-negative floats
+__device__ __forceinline__ float bound_max(float a, float b)
+{
+    return __uint_as_float(max(bound_bits(a), bound_bits(b)));
+}
+
+// sum / NaN-sticky maximum over aligned groups of N lanes (N a power of two <= 64)
+template <int N>
+__device__ __forceinline__ float group_sum(float v)
+{
+#pragma unroll
+    for (int off = N / 2; off >= 1; off >>= 1)
+        v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+template <int N>
+__device__ __forceinline__ float group_bound_max(float v)
+{
+#pragma unroll
+    for (int off = N / 2; off >= 1; off >>= 1)
+        v = bound_max(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
 __device__ __forceinline__ void flag_error(int32_t *dev_err, int32_t bit)
 {
     if (dev_err)

@@ -23,6 +23,8 @@ struct AppendArgs {
     void *v_data;
     int64_t v_stride_page, v_stride_head, v_stride_token;
     float k_scale, v_scale;
+    // per (page, KV head) bounds raised for every row written (null: none)
+    float *k_bounds, *v_bounds;
     const int32_t *slot_mapping;    // null: tail mode (below)
     int32_t *dev_err;
     // tail mode: token t = b * n_new + i goes to position seq_lens[b] - n_new + i
@@ -44,6 +46,10 @@ struct PartialArgs {
     const void *v_data;
     int64_t v_stride_page, v_stride_head, v_stride_token;
     float k_scale, v_scale;
+    // per (page, KV head) bounds: K row norms, V magnitudes (stored units).
+    // Both set: fixed-shift softmax where the gate allows; the single-launch
+    // step's append raises them for the rows it writes.
+    float *k_bounds, *v_bounds;
     const int32_t *block_table;
     int32_t max_pages;
     const int32_t *seq_lens;
@@ -118,6 +124,18 @@ struct MergeArgs {
 
 hipError_t launch_append(const AppendArgs &a, hipStream_t stream);
 hipError_t launch_lens_advance(int32_t *seq_lens, int32_t batch, int32_t n, hipStream_t stream);
+// bounds of both pools from the rows the sequences hold (zeroed first)
+struct BoundsArgs {
+    const void *k_data, *v_data;
+    int32_t dtype, num_pages, kv_heads, page_tokens, head_dim, v_head_dim;
+    int64_t k_stride_page, k_stride_head, k_stride_token;
+    int64_t v_stride_page, v_stride_head, v_stride_token;
+    float *k_bounds, *v_bounds;
+    const int32_t *block_table, *seq_lens;
+    int32_t max_pages, batch;
+    int32_t *dev_err;
+};
+hipError_t launch_kv_bounds(const BoundsArgs &a, hipStream_t stream);
 hipError_t launch_partial_valu(const PartialArgs &a, hipStream_t stream);
 hipError_t launch_partial_mfma(const PartialArgs &a, hipStream_t stream);
 // true when launch_partial_mfma runs `a` as one persistent launch, so that it

@@ -225,6 +225,109 @@ __device__ __forceinline__ void softmax_step(float (&sc)[2][4], float &m_run, fl
     }
 }
 
+// ------------------------------------------------------------------ fixed shift
+//
+// The fixed-shift softmax of the maxdiffusion PR #477 page (fixed-m splash
+// attention with dynamic bounds), in log2 units: a split whose keys have
+// norms <= kb, whose values (in the accumulator's units) are <= Vmax and
+// whose sequence holds N keys gets C = 127 - ceil(log2 N) - ceil(log2 Vmax)
+// and gate = floor((C + 125) / 2); a query row with norm |q| gets U = |scale|
+// |q| kb (an upper bound of every |score|, here enlarged by 2^-12 to cover
+// the rounding of the norms and of the fp32 dot product) and the shift
+// m = ceil(U) - C.  When ceil(U) <= gate every exponent score - m lies in
+// [-125, C]: no term leaves the normal fp32 range and N terms times Vmax
+// stay below 2^127, so p = 2^(score - m) is summed with no running maximum
+// and no rescaling.  Vmax = max(1, V bound * max(1, v_scale)) covers the
+// accumulator both before and after the V scale is applied.
+
+__device__ __forceinline__ int ceil_log2_count(int n)
+{
+    return n <= 1 ? 0 : 32 - __clz(n - 1);
+}
+
+// C and the gate for N keys and a V bound vb (false: the bound is not finite)
+__device__ __forceinline__ bool fixed_shift_consts(int n, float vb, float v_scale, int &C,
+                                                   int &gate)
+{
+    float vmax = vb * fmaxf(1.0f, v_scale);
+    if (!(vmax <= 3.0e38f))                    // NaN (unknown) or infinite
+        return false;
+    vmax = fmaxf(vmax, 1.0f);
+    int e;
+    const float f = frexpf(vmax, &e);          // vmax = f 2^e, f in [0.5, 1)
+    C = 127 - ceil_log2_count(n) - (f == 0.5f ? e - 1 : e);
+    const int W = C + 125;
+    gate = W >= 0 ? W / 2 : -((1 - W) / 2);    // floor(W / 2)
+    return true;
+}
+
+// The row's shift m (log2 units); true when the row passes the gate
+__device__ __forceinline__ bool fixed_shift_row(float q_norm, float kb, float scale_abs, int C,
+                                                int gate, float &m)
+{
+    const float U = scale_abs * q_norm * kb * (1.0f + 0x1p-12f);
+    const float cu = ceilf(U);
+    m = cu - (float)C;
+    return cu <= (float)gate;                  // false for NaN or infinite U
+}
+
+// Norm of this lane's query row from its bf16 operand registers (lane
+// 16 g + j holds columns 8 g .. 8 g + 7 of every 32-column k-step of row j)
+template <int KK>
+__device__ __forceinline__ float q_row_norm(const u32x4 (&qb)[KK])
+{
+    float ss = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float lo = __uint_as_float(qb[kk][w] << 16);
+            const float hi = __uint_as_float(qb[kk][w] & 0xFFFF0000u);
+            ss = fmaf(lo, lo, ss);
+            ss = fmaf(hi, hi, ss);
+        }
+    return sqrtf(xor_sum16_32(ss));
+}
+
+// Softmax step with a fixed shift m: p = 2^(s - m), l += sum p, no rescaling
+// (the P operands as softmax_step_n forms them)
+template <bool PVS, int NK>
+__device__ __forceinline__ void softmax_fixed_n(float (&sc)[2 * NK][4], float m, float &l_run,
+                                                u32x4 (&ph)[NK], u32x4 (&pl)[NK])
+{
+    float p[2 * NK][4], psum = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 2 * NK; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[t][i] = fast_exp2(sc[t][i] - m);
+            psum += p[t][i];
+        }
+    l_run += psum;
+#pragma unroll
+    for (int k = 0; k < NK; ++k)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int t = 2 * k + u;
+            ph[k][2 * u] = pack_bf16(p[t][0], p[t][1]);
+            ph[k][2 * u + 1] = pack_bf16(p[t][2], p[t][3]);
+            if constexpr (PVS) {
+                pl[k][2 * u] =
+                    pack_bf16(p[t][0] - bf16_round(p[t][0]), p[t][1] - bf16_round(p[t][1]));
+                pl[k][2 * u + 1] =
+                    pack_bf16(p[t][2] - bf16_round(p[t][2]), p[t][3] - bf16_round(p[t][3]));
+            }
+        }
+}
+
+// m_part of a row: the fixed shift (no key: -inf) or the running maximum
+__device__ __forceinline__ float stored_m(bool fixed, float m_fix, float m_run, float l_total)
+{
+    if (fixed)
+        return l_total > 0.0f ? m_fix * kLn2 : -INFINITY;
+    return m_run == -INFINITY ? -INFINITY : m_run * kLn2;
+}
+
 // ------------------------------------------------------------------ decode
 
 template <int D, int DV, int KVT, bool PVS, int PG>
@@ -457,26 +560,35 @@ decode_mfma_kernel(PartialArgs a)
 // conversions: bf16 -> bf16 bit copy, fp32 -> bf16 round to nearest even, to
 // fp8 the correctly rounded quotient value / scale, rounded to nearest even
 // and saturated.  Lane l stores elements l * D/64 .. (l + 1) * D/64 - 1.
-template <int D, int KVT>
-__device__ __forceinline__ void store_new_row(const void *src_base, int src_dtype, int64_t src,
-                                              void *pool, int64_t dst, float scale, int lane)
+// Returns the lane's share of the stored row's bound statistic (stored
+// units): the sum of squares (K) or the largest magnitude (V).
+template <int D, int KVT, bool V>
+__device__ __forceinline__ float store_new_row(const void *src_base, int src_dtype, int64_t src,
+                                               void *pool, int64_t dst, float scale, int lane)
 {
     constexpr int E = D / 64;
+    float stat = 0.0f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         const int64_t i = lane * E + e;
+        float stored;
         if constexpr (KVT == NBX_BF16) {
             const uint16_t bits = src_dtype == NBX_BF16
                                       ? ((const uint16_t *)src_base)[src + i]
                                       : f32_to_bf16_bits(((const float *)src_base)[src + i]);
             ((uint16_t *)pool)[dst + i] = bits;
+            stored = bf16_bits_to_f32(bits);
         } else {
             const float x = src_dtype == NBX_BF16
                                 ? bf16_bits_to_f32(((const uint16_t *)src_base)[src + i])
                                 : ((const float *)src_base)[src + i];
-            ((uint8_t *)pool)[dst + i] = f32_to_e4m3(__fdiv_rn(x, scale));
+            const uint8_t code = f32_to_e4m3(__fdiv_rn(x, scale));
+            ((uint8_t *)pool)[dst + i] = code;
+            stored = e4m3_to_f32(code);
         }
+        stat = V ? bound_max(stat, fabsf(stored)) : fmaf(stored, stored, stat);
     }
+    return stat;
 }
 
 constexpr int kPersistMaxBatch = 256;      // sequences covered by the lane-register item table
@@ -490,9 +602,14 @@ constexpr int kPersistMaxBatch = 256;      // sequences covered by the lane-regi
 // chunk's loads (and, one chunk ahead of an item boundary, the next item's Q
 // and page ids) in flight while the current chunk is computed, so the cost of
 // starting a wave is paid once, not once per split.  Splits without keys get
-// m = -inf and l = 0; their o is not written.
-template <int D, int DV, int KVT, bool PVS, int NB, bool FA>
-__global__ void __launch_bounds__(64)
+// m = -inf and l = 0; their o is not written.  BND: a pool carries bounds
+// (raised by the fused append; with both, the fixed-shift softmax), a
+// separate instantiation so that the plain kernel keeps its registers; at
+// D = 128 it is held to 2 waves per SIMD like the plain one (it fits 256
+// registers without spilling; left to itself the compiler takes one more
+// AGPR block and halves the resident waves).
+template <int D, int DV, int KVT, bool PVS, int NB, bool FA, bool BND>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu((BND && D == 128) ? 2 : 1)))
 decode_persistent_kernel(PartialArgs a)
 {
     constexpr int KK = D / 32, DT = DV / 16;
@@ -588,7 +705,10 @@ decode_persistent_kernel(PartialArgs a)
     struct Item {
         int b, gk, s, j0, jend, e_j, nchunk, L;
         int64_t row_base;
+        float kb, vb;                          // K norm / V magnitude bounds of its pages
     };
+    // fixed-shift softmax: both pools carry per-page bounds
+    const bool use_bounds = BND && a.k_bounds != nullptr && a.v_bounds != nullptr;
     auto make_item = [&](int k) {
         Item it;
         int before = 0;                        // sequences whose items all precede k
@@ -608,6 +728,19 @@ decode_persistent_kernel(PartialArgs a)
         it.e_j = min(it.jend, n_j);
         it.row_base = ((int64_t)it.b * a.q_heads + (int64_t)it.gk * a.group) * a.q_rows;
         it.L = L;
+        it.kb = it.vb = 0.0f;
+        if (use_bounds) {                      // the bounds of the pages the item reads
+            const int T = a.page_tokens;
+            for (int pi = it.j0 / T + lane; pi <= (it.jend - 1) / T; pi += 64) {
+                const int page = a.block_table[(int64_t)it.b * a.max_pages + pi];
+                if (page >= 0 && page < a.num_pages) {
+                    it.kb = bound_max(it.kb, a.k_bounds[(int64_t)page * H + it.gk]);
+                    it.vb = bound_max(it.vb, a.v_bounds[(int64_t)page * H + it.gk]);
+                }
+            }
+            it.kb = group_bound_max<64>(it.kb);
+            it.vb = group_bound_max<64>(it.vb);
+        }
         return it;
     };
     // Fused append: the new positions L - n_new .. L - 1 that fall in the item
@@ -616,7 +749,8 @@ decode_persistent_kernel(PartialArgs a)
     // and a wave's memory operations are performed in order, so its later
     // tile loads see the new rows.
     // `pg` holds the page ids of the item's first 32 chunks (item_pages(it, 0)).
-    auto append_item = [&](const Item &it, int pg) {
+    // With bounds, each written row raises its page's bound and the item's.
+    auto append_item = [&](Item &it, int pg) {
         if constexpr (FA) {
             const int first = it.L - a.n_new;
             const int lo = max(it.j0, max(first, 0)), hi = min(it.j0 + S, it.L);
@@ -628,14 +762,24 @@ decode_persistent_kernel(PartialArgs a)
                     continue;
                 const int64_t src = ((int64_t)it.b * a.n_new + (p - first)) * H + it.gk;
                 const int64_t r = p % a.page_tokens;
-                store_new_row<D, KVT>(a.new_k, a.new_dtype, src * D, (void *)a.k_data,
-                                      (int64_t)page * a.k_stride_page + it.gk * a.k_stride_head +
-                                          r * a.k_stride_token,
-                                      a.k_scale, lane);
-                store_new_row<DV, KVT>(a.new_v, a.new_dtype, src * DV, (void *)a.v_data,
-                                       (int64_t)page * a.v_stride_page + it.gk * a.v_stride_head +
-                                           r * a.v_stride_token,
-                                       a.v_scale, lane);
+                const float ks = store_new_row<D, KVT, false>(
+                    a.new_k, a.new_dtype, src * D, (void *)a.k_data,
+                    (int64_t)page * a.k_stride_page + it.gk * a.k_stride_head + r * a.k_stride_token,
+                    a.k_scale, lane);
+                const float vs_ = store_new_row<DV, KVT, true>(
+                    a.new_v, a.new_dtype, src * DV, (void *)a.v_data,
+                    (int64_t)page * a.v_stride_page + it.gk * a.v_stride_head + r * a.v_stride_token,
+                    a.v_scale, lane);
+                if (BND && (a.k_bounds || a.v_bounds)) {
+                    const float kn = sqrtf(group_sum<64>(ks)), vm = group_bound_max<64>(vs_);
+                    const int64_t bi = (int64_t)page * H + it.gk;
+                    if (a.k_bounds && lane == 0)
+                        raise_bound(a.k_bounds, bi, kn);
+                    if (a.v_bounds && lane == 0)
+                        raise_bound(a.v_bounds, bi, vm);
+                    it.kb = bound_max(it.kb, kn);
+                    it.vb = bound_max(it.vb, vm);
+                }
             }
             asm volatile("" ::: "memory");     // keep the tile loads after the stores
         }
@@ -712,6 +856,8 @@ decode_persistent_kernel(PartialArgs a)
     };
 
     float m_run = -INFINITY, l_run = 0.0f;
+    bool fixed = false;                        // the item being computed uses a fixed shift
+    float m_fix = 0.0f;                        // its shift for this lane's row (log2 units)
     f32x4 o[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -778,13 +924,26 @@ decode_persistent_kernel(PartialArgs a)
                 sc[t][i] = (tv && pos < ci.e_j) ? acc[i] * scale2 : -INFINITY;
             }
         }
+        if (use_bounds && cc == 0) {           // the item's Q is still in qb
+            int C, gate;
+            bool ok = fixed_shift_consts(ci.L, ci.vb, vs, C, gate);
+            ok = ok && fixed_shift_row(q_row_norm<KK>(qb), ci.kb, fabsf(scale2), C, gate, m_fix);
+            fixed = __all(ok);
+        }
         if (more) {
             issue_k(cur, c, pg0, pg1);
             if (c == cur.nchunk - 1)
                 prepare_next();
         }
         u32x4 ph, pl;
-        softmax_step<DT, PVS>(sc, m_run, l_run, o, ph, pl);
+        if (BND && fixed) {
+            u32x4 ph1[1], pl1[1];
+            softmax_fixed_n<PVS, 1>(sc, m_fix, l_run, ph1, pl1);
+            ph = ph1[0];
+            pl = pl1[0];
+        } else {
+            softmax_step<DT, PVS>(sc, m_run, l_run, o, ph, pl);
+        }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
             const u32x4 va = vt_operand<DT>(vt_lane, dt);
@@ -801,7 +960,7 @@ decode_persistent_kernel(PartialArgs a)
                 for (int dt = 0; dt < DT; ++dt)
                     *(f32x4 *)(op + dt * 16 + 4 * g) = o[dt] * vs;
                 if (g == 0) {
-                    a.m_part[row * NS + ci.s] = m_run == -INFINITY ? -INFINITY : m_run * kLn2;
+                    a.m_part[row * NS + ci.s] = stored_m(BND && fixed, m_fix, m_run, lt);
                     a.l_part[row * NS + ci.s] = lt;
                 }
             }
@@ -905,6 +1064,35 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
             o[n][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    // fixed-shift softmax where both pools carry bounds: per row tile, a shift
+    // per row and one decision for the tile's 16 rows
+    bool fixed[NT];
+    float m_fix[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        fixed[n] = false;
+        m_fix[n] = 0.0f;
+    }
+    if (a.k_bounds != nullptr && a.v_bounds != nullptr && nchunk > 0) {
+        float kb = 0.0f, vb = 0.0f;
+        const int T = a.page_tokens;
+        for (int pi = j0 / T + lane; pi <= (jend - 1) / T; pi += 64) {
+            const int page = a.block_table[(int64_t)b * a.max_pages + pi];
+            if (page >= 0 && page < a.num_pages) {
+                kb = bound_max(kb, a.k_bounds[(int64_t)page * a.kv_heads + gk]);
+                vb = bound_max(vb, a.v_bounds[(int64_t)page * a.kv_heads + gk]);
+            }
+        }
+        kb = group_bound_max<64>(kb);
+        vb = group_bound_max<64>(vb);
+        int C, gate;
+        if (fixed_shift_consts(L, vb, a.v_scale, C, gate)) {
+#pragma unroll
+            for (int n = 0; n < NT; ++n)
+                fixed[n] = __all(fixed_shift_row(q_row_norm<KK>(qb[n]), kb, fabsf(scale2), C, gate,
+                                                 m_fix[n]));
+        }
     }
 
     const int64_t k_head = (int64_t)gk * a.k_stride_head;
@@ -1037,7 +1225,10 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
                     sc[t][i] = (ok[t] && pos < e_n) ? acc[n][t][i] * scale2 : -INFINITY;
                 }
             }
-            softmax_step_n<DT, PVS, NK>(sc, m_run[n], l_run[n], o[n], ph[n], pl[n]);
+            if (fixed[n])
+                softmax_fixed_n<PVS, NK>(sc, m_fix[n], l_run[n], ph[n], pl[n]);
+            else
+                softmax_step_n<DT, PVS, NK>(sc, m_run[n], l_run[n], o[n], ph[n], pl[n]);
         }
 #pragma unroll
         for (int kq = 0; kq < NK; ++kq)
@@ -1097,7 +1288,7 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
             for (int dt = 0; dt < DT; ++dt)
                 *(f32x4 *)(op + dt * 16 + 4 * g) = o[n][dt] * vs;
             if (g == 0) {
-                a.m_part[row * a.n_split + s] = m_run[n] == -INFINITY ? -INFINITY : m_run[n] * kLn2;
+                a.m_part[row * a.n_split + s] = stored_m(fixed[n], m_fix[n], m_run[n], lt);
                 a.l_part[row * a.n_split + s] = lt;
             }
         }
@@ -1112,7 +1303,7 @@ constexpr int kMrNK = 2, kMrNSet = 1;
 
 // Waves the current device holds at once for the persistent decode kernel
 // (resident workgroups per CU x CUs), cached per device.
-template <int D, int DV, int KVT, bool PVS, int NB, bool FA>
+template <int D, int DV, int KVT, bool PVS, int NB, bool FA, bool BND>
 int persistent_waves()
 {
     constexpr int kMaxDev = 64;
@@ -1128,7 +1319,8 @@ int persistent_waves()
     int per_cu = 0, cus = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &per_cu,
-            reinterpret_cast<const void *>(&decode_persistent_kernel<D, DV, KVT, PVS, NB, FA>), 64,
+            reinterpret_cast<const void *>(&decode_persistent_kernel<D, DV, KVT, PVS, NB, FA, BND>),
+            64,
             0) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return 0;
@@ -1138,16 +1330,16 @@ int persistent_waves()
     return v;
 }
 
-template <int D, int DV, int KVT, bool PVS, int NB, bool FA>
+template <int D, int DV, int KVT, bool PVS, int NB, bool FA, bool BND>
 hipError_t launch_persistent(const PartialArgs &a, hipStream_t stream)
 {
     const int64_t items = (int64_t)a.batch * a.kv_heads * a.n_split;
-    const int waves = persistent_waves<D, DV, KVT, PVS, NB, FA>();
+    const int waves = persistent_waves<D, DV, KVT, PVS, NB, FA, BND>();
     if (waves <= 0)
         return hipErrorInvalidConfiguration;
     const int grid = (int)(items < waves ? items : waves);
-    hipLaunchKernelGGL((decode_persistent_kernel<D, DV, KVT, PVS, NB, FA>), dim3(grid), dim3(64),
-                       0, stream, a);
+    hipLaunchKernelGGL((decode_persistent_kernel<D, DV, KVT, PVS, NB, FA, BND>), dim3(grid),
+                       dim3(64), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1162,11 +1354,17 @@ hipError_t launch_kind(const PartialArgs &a, hipStream_t stream)
     const int M = a.rows_per_kv;
     if (persistent_shape(a)) {
         const bool fa = a.new_k != nullptr && a.n_new > 0;
+        // bounds matter to the fused append (any pool) and to the reads (both)
+        const bool bnd = fa ? (a.k_bounds || a.v_bounds) : (a.k_bounds && a.v_bounds);
+#define NBX_PERSIST(NB_)                                                                        \
+    (fa ? (bnd ? launch_persistent<D, DV, KVT, PVS, NB_, true, true>(a, stream)                 \
+               : launch_persistent<D, DV, KVT, PVS, NB_, true, false>(a, stream))               \
+        : (bnd ? launch_persistent<D, DV, KVT, PVS, NB_, false, true>(a, stream)                \
+               : launch_persistent<D, DV, KVT, PVS, NB_, false, false>(a, stream)))
         if (a.batch <= 64)
-            return fa ? launch_persistent<D, DV, KVT, PVS, 1, true>(a, stream)
-                      : launch_persistent<D, DV, KVT, PVS, 1, false>(a, stream);
-        return fa ? launch_persistent<D, DV, KVT, PVS, 4, true>(a, stream)
-                  : launch_persistent<D, DV, KVT, PVS, 4, false>(a, stream);
+            return NBX_PERSIST(1);
+        return NBX_PERSIST(4);
+#undef NBX_PERSIST
     }
     if (a.new_k != nullptr && a.n_new > 0)
         return hipErrorInvalidValue;           // the caller appends first for these shapes

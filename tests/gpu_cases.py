@@ -24,9 +24,25 @@ class DevCase:
         self.slots = (torch.from_numpy(case.slot_mapping).to(device)
                       if case.slot_mapping is not None else None)
         self.err = torch.zeros(1, dtype=torch.int32, device=device)
+        self.kb = self.vb = None               # per-page bounds (fixed-shift softmax)
 
     def pools(self):
-        return nb.KVPool(self.k, self.case.k_scale), nb.KVPool(self.v, self.case.v_scale)
+        return (nb.KVPool(self.k, self.case.k_scale, self.kb),
+                nb.KVPool(self.v, self.case.v_scale, self.vb))
+
+    def attach_bounds(self, lens=None):
+        """Allocate per-page bounds for both pools and compute them with
+        nbx_paged_kv_bounds over the rows of `lens` (default: the case's lengths)."""
+        P, H = self.k.shape[0], self.k.shape[1]
+        self.kb = torch.full((P, H), -1.0, device=self.k.device)   # overwritten by the call
+        self.vb = torch.full((P, H), -1.0, device=self.k.device)
+        lens_d = self.lens if lens is None else torch.as_tensor(
+            np.asarray(lens, dtype=np.int32)).to(self.k.device)
+        kp, vp = self.pools()
+        nb.nbx_paged_kv_bounds(kp, vp, self.bt, lens_d, dev_err=self.err)
+
+    def detach_bounds(self):
+        self.kb = self.vb = None
 
     def plan(self):
         return nb.case_plan(self.case)

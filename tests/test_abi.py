@@ -21,7 +21,7 @@ def test_every_declared_symbol_is_exported(lib):
             "nbx_paged_decode", "nbx_paged_decode_plan", "nbx_paged_decode_workspace_bytes",
             "nbx_status_str", "nbx_version", "nbx_paged_decode_step",
             "nbx_paged_lens_advance", "nbx_paged_decode_partial_windows",
-            "nbx_paged_decode_plan_rows"} <= set(names)
+            "nbx_paged_decode_plan_rows", "nbx_paged_kv_bounds"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -148,6 +148,19 @@ def test_append_validation(lib):
     assert f(vp=pool(num_pages=9)) == -3
     assert f(kp=wide(192), vp=wide(128), sh=192, st=384) == -3   # one call per pool width
     assert f(n=0) == 0                           # no-op, nothing launched
+
+
+def test_bounds_validation(lib):
+    kb = FAKE + 4096
+    f = lambda kp, vp, bt=FAKE, mp=4, sl=FAKE, b=2: lib.nbx_paged_kv_bounds(
+        ctypes.byref(kp), ctypes.byref(vp), bt, mp, sl, b, None, None)
+    assert f(pool(), pool(bounds=kb)) == -1                 # K pool without bounds
+    assert f(pool(bounds=kb), pool()) == -1
+    assert f(pool(bounds=kb), pool(bounds=kb), bt=None) == -1
+    assert f(pool(bounds=kb + 2), pool(bounds=kb)) == -4    # misaligned bounds
+    assert f(pool(bounds=kb), pool(bounds=kb, kv_heads=4)) == -3
+    assert f(pool(bounds=kb), pool(bounds=kb), b=-1) == -3
+    assert f(pool(bounds=kb), pool(bounds=kb), mp=70000) == -6
 
 
 def test_merge_validation(lib):
