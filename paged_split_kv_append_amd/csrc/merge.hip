@@ -10,7 +10,9 @@
 // D/4).  A lane takes 4 consecutive columns of one split, so a wave covers
 // 256 / (D/4) splits per pass; with up to 64 splits every load of the row
 // (m, l and all o pieces) is issued at once and the row takes one memory
-// round trip.  Each lane sums its splits in ascending order, then the lanes
+// round trip.  The number of passes is a template argument, the fewest that
+// cover the launch's split count, so that no load is issued for splits that
+// do not exist.  Each lane sums its splits in ascending order, then the lanes
 // holding different splits of the same columns are added by a fixed butterfly
 // (and the denominator by a wave butterfly), so the order is fixed and
 // repeated runs give identical bits.  No LDS and no barrier: the four waves
@@ -30,14 +32,14 @@ __device__ __forceinline__ float4 fma4(float w, float4 v, float4 acc)
                        fmaf(w, v.w, acc.w));
 }
 
-template <int D, int OUT>
+template <int D, int OUT, int NP>
 __global__ void __launch_bounds__(256)
 merge_kernel(MergeArgs a)
 {
     constexpr int CW = D / 4;                  // columns per wave
     constexpr int LPS = CW / 4;                // lanes per split (4 columns each)
     constexpr int SPP = 64 / LPS;              // splits per pass
-    constexpr int NP = LPS;                    // passes in flight: SPP * NP = 64 splits
+    static_assert(NP >= 1 && NP <= LPS, "at most 64 splits in flight");
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int64_t row = blockIdx.x;
     const int ns = a.n_split;
@@ -136,16 +138,37 @@ merge_kernel(MergeArgs a)
     }
 }
 
+// passes: the fewest powers of two that cover n_split splits at SPP splits per
+// pass, at most the 64-split one-round-trip form (more splits loop over it)
+template <int D, int OUT>
+hipError_t launch_np(const MergeArgs &a, hipStream_t stream)
+{
+    constexpr int LPS = D / 16, SPP = 64 / LPS;
+    dim3 grid((unsigned)a.rows);
+    const int need = (a.n_split + SPP - 1) / SPP;
+    if (need <= 1)
+        hipLaunchKernelGGL((merge_kernel<D, OUT, 1>), grid, dim3(256), 0, stream, a);
+    else if (need <= 2)
+        hipLaunchKernelGGL((merge_kernel<D, OUT, 2>), grid, dim3(256), 0, stream, a);
+    else if (need <= 4 || LPS == 4)
+        hipLaunchKernelGGL((merge_kernel<D, OUT, (LPS < 4 ? LPS : 4)>), grid, dim3(256), 0, stream,
+                           a);
+    else if (need <= 8 || LPS == 8)
+        hipLaunchKernelGGL((merge_kernel<D, OUT, (LPS < 8 ? LPS : 8)>), grid, dim3(256), 0, stream,
+                           a);
+    else
+        hipLaunchKernelGGL((merge_kernel<D, OUT, LPS>), grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
 template <int OUT>
 hipError_t launch_out(const MergeArgs &a, hipStream_t stream)
 {
-    dim3 grid((unsigned)a.rows);
     switch (a.head_dim) {
-    case 64: hipLaunchKernelGGL((merge_kernel<64, OUT>), grid, dim3(256), 0, stream, a); break;
-    case 128: hipLaunchKernelGGL((merge_kernel<128, OUT>), grid, dim3(256), 0, stream, a); break;
-    default: hipLaunchKernelGGL((merge_kernel<256, OUT>), grid, dim3(256), 0, stream, a); break;
+    case 64: return launch_np<64, OUT>(a, stream);
+    case 128: return launch_np<128, OUT>(a, stream);
+    default: return launch_np<256, OUT>(a, stream);
     }
-    return hipGetLastError();
 }
 
 }  // namespace
