@@ -33,9 +33,6 @@ __device__ u32x4 nbx_buffer_load_b128(i32x4 rsrc, int voffset, int soffset, int 
     __asm("llvm.amdgcn.raw.buffer.load.v4i32");
 __device__ u32x2 nbx_buffer_load_b64(i32x4 rsrc, int voffset, int soffset, int aux)
     __asm("llvm.amdgcn.raw.buffer.load.v2i32");
-__device__ void nbx_buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) void *lds,
-                                    int size, int voffset, int soffset, int imm_offset, int aux)
-    __asm("llvm.amdgcn.raw.buffer.load.lds");
 
 // Descriptor for `bytes` bytes from `base` (uniform values; forced to SGPRs).
 __device__ __forceinline__ i32x4 make_buffer_rsrc(const void *base, uint32_t bytes)
@@ -116,22 +113,6 @@ __device__ __forceinline__ float bf16_round(float x)
 __device__ __forceinline__ float fast_exp2(float x)
 {
     return __builtin_amdgcn_exp2f(x);
-}
-
-// A-operand of the P V product (V^T, 16 columns of V x 32 positions) from a
-// row-major bf16 tile in LDS: rows are positions, `stride` bytes apart.
-// Lane 16 g + j gets V[4 g + t][c0 + j] (t = 0..3) and V[16 + 4 g + t][c0 + j].
-__device__ __forceinline__ u32x4 lds_vt_operand(const uint8_t *tile, int stride, int c0, int lane)
-{
-    const int g = lane >> 4, j = lane & 15;
-    const uint8_t *p0 = tile + (4 * g + (j >> 2)) * stride + (c0 + 4 * (j & 3)) * 2;
-    const uint8_t *p1 = p0 + 16 * stride;
-    const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (lds_bf16x4 *)(__attribute__((address_space(3))) uint8_t *)p0);
-    const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (lds_bf16x4 *)(__attribute__((address_space(3))) uint8_t *)p1);
-    const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
-    return u32x4{ua[0], ua[1], ub[0], ub[1]};
 }
 
 __device__ __forceinline__ float xor_max16_32(float v)

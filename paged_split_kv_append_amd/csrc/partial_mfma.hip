@@ -181,48 +181,16 @@ __device__ __forceinline__ void softmax_step_n(float (&sc)[2 * NK][4], float &m_
         }
 }
 
-// Online-softmax step for one lane's row over the 32 positions of a chunk:
-// sc holds the scaled scores (log2 units, -inf where masked).  Updates m, l,
-// rescales o and returns the P operand (hi and residual lo parts).
+// Online-softmax step for one lane's row over the 32 positions of a chunk
+// (softmax_step_n with one k-step): returns the P operand (hi and residual lo).
 template <int DT, bool PVS>
 __device__ __forceinline__ void softmax_step(float (&sc)[2][4], float &m_run, float &l_run,
                                              f32x4 (&o)[DT], u32x4 &ph, u32x4 &pl)
 {
-    float mx = sc[0][0];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            mx = fmaxf(mx, sc[t][i]);
-    mx = xor_max16_32(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_safe = m_new == -INFINITY ? 0.0f : m_new;
-    const float corr = fast_exp2(m_run - m_safe);
-    float p[2][4], psum = 0.0f;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            p[t][i] = fast_exp2(sc[t][i] - m_safe);
-            psum += p[t][i];
-        }
-    l_run = l_run * corr + psum;
-    m_run = m_new;
-    if (__any(corr != 1.0f)) {             // a row's max moved: rescale (else o * 1 = o)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-            o[dt] *= corr;
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        ph[2 * t] = pack_bf16(p[t][0], p[t][1]);
-        ph[2 * t + 1] = pack_bf16(p[t][2], p[t][3]);
-        if constexpr (PVS) {
-            pl[2 * t] = pack_bf16(p[t][0] - bf16_round(p[t][0]), p[t][1] - bf16_round(p[t][1]));
-            pl[2 * t + 1] =
-                pack_bf16(p[t][2] - bf16_round(p[t][2]), p[t][3] - bf16_round(p[t][3]));
-        }
-    }
+    u32x4 ph1[1], pl1[1];
+    softmax_step_n<DT, PVS, 1>(sc, m_run, l_run, o, ph1, pl1);
+    ph = ph1[0];
+    pl = pl1[0];
 }
 
 // ------------------------------------------------------------------ fixed shift

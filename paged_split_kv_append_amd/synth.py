@@ -123,9 +123,10 @@ def _draw_lens(spec, batch, rng):
     kind = spec[0]
     if kind == "fixed":
         return np.full(batch, spec[1], dtype=np.int64)
-    if kind == "uniform":
+    if kind == "uniform":                      # ("uniform", lo, hi[, step]): multiples of step
         lo, hi = spec[1], spec[2]
-        return rng.integers(lo, hi + 1, size=batch, dtype=np.int64)
+        step = spec[3] if len(spec) > 3 else 1
+        return rng.integers(-(-lo // step), hi // step + 1, size=batch, dtype=np.int64) * step
     if kind == "loguniform":
         lo, hi = spec[1], spec[2]
         x = np.floor(np.exp(rng.uniform(math.log(lo), math.log(hi), size=batch)))
