@@ -256,6 +256,26 @@ def test_zero_length_sequence_gives_zero_rows():
     assert max_abs(out, ref) <= TOL["bf16"]
 
 
+# ------------------------------------------------------------------ large batches
+
+@pytest.mark.parametrize("kv_dtype,split", [("bf16", 64), ("bf16", 256), ("bf16", 1024),
+                                            ("fp8", 256)])
+def test_batch_beyond_the_persistent_table(kv_dtype, split):
+    """More than 256 sequences: one workgroup per (split, sequence x KV head) with
+    1, 2 or 4 waves taking interleaved chunks of the split (by split length)."""
+    case = synth.make_case(2, seed=68, append=False, batch=300, lens=("uniform", 1, 1000),
+                           kv_dtype=kv_dtype)
+    print(f"batch 300 {kv_dtype} split {split}", flush=True)
+    dc = DevCase(case)
+    n_split = -(-int(case.seq_lens.max()) // split)
+    out = dc.decode(n_split=n_split, split_size=split)
+    torch.cuda.synchronize()
+    ref, _, _ = _reference(case, dc)
+    assert dc.err_bits() == 0
+    assert torch.isfinite(out).all()
+    assert max_abs(out, ref) <= TOL[kv_dtype]
+
+
 # ------------------------------------------------------------------ full sizes
 
 FULL_ROWS = {2: None, 5: None, 3: [(0, 48), (1488, 1536)], 4: [(0, 32), (3040, 3072)]}

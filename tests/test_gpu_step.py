@@ -270,10 +270,12 @@ def test_lens_advance():
     assert lens.tolist() == [3, 8, 103, 10]
 
 
-def test_step_graph_replays_as_lengths_grow():
+@pytest.mark.parametrize("bounds", [False, True], ids=["running_max", "fixed_shift"])
+def test_step_graph_replays_as_lengths_grow(bounds):
     """One recorded graph of [lens advance, step with a device-derived split]
     replayed for four tokens: every replay appends at the new last position and
-    attends to it, with the launch arguments unchanged."""
+    attends to it, with the launch arguments unchanged.  With pool bounds the
+    append inside the step raises them and the reads take the fixed shift."""
     steps = 4
     case = synth.make_case(2, seed=71, append=False, batch=5, lens=("uniform", 40, 600))
     final = case.seq_lens.copy()
@@ -294,6 +296,8 @@ def test_step_graph_replays_as_lengths_grow():
 
     dc = DevCase(case)
     dc.lens.copy_(torch.from_numpy(start))
+    if bounds:
+        dc.attach_bounds(lens=start)
     kp, vp = dc.pools()
     ws = torch.zeros(nb.nbx_paged_decode_workspace_bytes(case.rows, n_split, D),
                      dtype=torch.uint8, device="cuda")
@@ -325,6 +329,17 @@ def test_step_graph_replays_as_lengths_grow():
         assert dc.err_bits() == 0
         assert torch.isfinite(out).all()
         assert max_abs(out.reshape(case.rows, D), ref) <= TOL["bf16"]
+    if bounds:
+        # every split of the last replay took a fixed shift (an integer in log2 units)
+        _, m, l = nb.workspace_partials(ws, case.rows, n_split, D)
+        m_np, l_np = m.double().cpu().numpy(), l.double().cpu().numpy()
+        kq = m_np[l_np > 0] / np.log(2.0)
+        assert kq.size and np.all(np.abs(kq - np.round(kq)) < 1e-4)
+        # the bounds cover the appended rows: equal to the oracle's over the final lengths
+        rk = oracle.kv_bounds(k_ref, case.kv_dtype, case.block_table, final, is_value=False)
+        rv = oracle.kv_bounds(v_ref, case.kv_dtype, case.block_table, final, is_value=True)
+        gk, gv = dc.kb.double().cpu().numpy(), dc.vb.double().cpu().numpy()
+        assert np.all(np.abs(gk - rk) <= 1e-5 * rk) and np.array_equal(gv, rv)
 
 
 def test_prompt_chunk_chain_over_a_growing_cache():
