@@ -19,7 +19,7 @@
  *   the split kernel on the nbxtensor paged_decode_attn.py page); outputs
  *   and partial outputs have Dv columns.  The keys are cut into splits of split_size
  *   positions; each split yields an unnormalised partial (o, m, l) with an
- *   fp32 accumulator, and the partials are merged in ascending split order.
+ *   fp32 accumulator, and the partials are merged in a fixed order.
  *
  * Conventions shared by every entry point:
  *
@@ -278,7 +278,9 @@ int nbx_paged_decode_partial_windows(const void *q, int32_t q_dtype, int32_t bat
  * non-empty splits (m_s != -inf; the o of an empty split is not read),
  * w_s = exp(m_s - M), and
  *   out = sum_s w_s o_s / sum_s w_s l_s,
- * summed in ascending s.  A row with no non-empty split is 0.  NaN in a
+ * summed in a fixed order that depends only on n_split (each group of splits
+ * in ascending s, the groups then added pairwise in a fixed tree), so repeated
+ * calls give identical bits.  A row with no non-empty split is 0.  NaN in a
  * partial propagates to the row.
  *
  *   o_part, m_part, l_part  as written by nbx_paged_decode_partial.
