@@ -89,12 +89,21 @@ PARTIAL_SOURCES = ("paged_split_kv_append_amd/csrc/partial_mfma.hip",
                    "paged_split_kv_append_amd/csrc/partial_valu.hip")
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and with whitespace collapsed, so that a
+    comment edit does not count as a kernel change."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def partial_source_hash() -> str:
     import hashlib
     h = hashlib.sha256()
     for rel in PARTIAL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

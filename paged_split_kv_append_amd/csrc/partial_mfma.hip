@@ -12,10 +12,10 @@
 // Products are v_mfma_f32_16x16x32_bf16 with fp32 accumulation:
 //   S^T (16 positions x 16 rows) = K (16 x D) . Q^T (D x 16)
 //   O^T (16 columns x 16 rows) += V^T (16 x 32 positions) . P^T (32 x 16)
-// D is the q/k head dim and DV the V head dim (the width of o; the two differ
-// for latent-attention heads, e.g. 192 / 128).
 // so that every lane owns one query row (its column) in both S^T and O^T and
-// the softmax bookkeeping never leaves the lane's row.  bf16 K/V products are
+// the softmax bookkeeping never leaves the lane's row.  D is the q/k head dim
+// and DV the V head dim (the width of o; they differ for latent-attention
+// heads, e.g. 192 / 128).  bf16 K/V products are
 // exact; P is rounded to bf16 for the P V product, and for bf16 pools the
 // rounding residual is multiplied in a second MFMA (P = hi + lo, relative
 // error about 2^-17).  fp8 codes are widened to bf16 exactly; the K scale is
@@ -36,14 +36,18 @@
 // constant offset from one per-lane address.  Page ids come from the block
 // table once per 32 chunks (one per lane) and are broadcast with readlane.
 //
-// Two kernels:
-//  - decode_mfma_kernel: at most 16 rows per KV head (decode, short windows).
-//    PG waves per (split, sequence x KV head) take interleaved chunks of the
-//    split, each with its own (m, l, O), combined in a fixed order at the end.
-//    K rows go from HBM straight into MFMA operand registers; V rows are
-//    loaded into registers and written to the wave's LDS tile once they land
-//    (fp8 codes widened on the way).  The wave's next chunk is loaded while
-//    the current one is computed.
+// Three kernels:
+//  - decode_persistent_kernel: at most 16 rows per KV head (decode, short
+//    windows) and at most 256 sequences; one wave per (sequence, split, KV
+//    head) item, as many waves as the device holds, items enumerated on the
+//    device, the step's append fused in (described at the kernel).
+//  - decode_mfma_kernel: the same rows for larger batches.  PG waves per
+//    (split, sequence x KV head) take interleaved chunks of the split, each
+//    with its own (m, l, O), combined in a fixed order at the end.
+//    In both decode kernels K rows go from HBM straight into MFMA operand
+//    registers; V rows are loaded into registers and written to the wave's
+//    LDS tile once they land (fp8 codes widened on the way).  The wave's next
+//    chunk is loaded while the current one is computed.
 //  - multirow_mfma_kernel: more rows per KV head (verify windows, prompt
 //    chunks).  A workgroup takes RW x NT row tiles of 16 rows; its waves share
 //    the loads of each K and V chunk and stage it in LDS (K column-blocked by
@@ -52,6 +56,8 @@
 //    Workgroups are ordered row block fastest and mapped so that the row
 //    blocks of one split run on the same XCD and share its L2 (the rows-first
 //    order of TensorFold PR #1219, made XCD-aware).
+// The persistent and multi-row kernels also take the fixed-shift softmax
+// when both pools carry per-page bounds (see "fixed shift" below).
 #include <atomic>
 
 #include "kernels.h"
@@ -949,9 +955,9 @@ decode_persistent_kernel(PartialArgs a)
 // KV head, split).  The K and V tiles of a chunk are pieces of 1 KB (as bf16:
 // 16 rows x 32 columns); waves 0-3 load the K pieces and waves 4-7 the V
 // pieces, each wave all its pieces from one tile, so each of its loads has a
-// fixed role (K or V, tile) and one descriptor per tile serves it.  Chunk c + 1 waits in LDS
-// and chunks c + 2, c + 3 in registers while chunk c is computed; one barrier
-// per chunk.  K is stored in LDS with a 16-byte swizzle inside each 1 KB
+// fixed role (K or V, tile) and one descriptor per tile serves it.  Chunk c + 1
+// waits in LDS and chunks c + 2 ... c + 1 + NSET in registers while chunk c is
+// computed; one barrier per chunk.  K is stored in LDS with a 16-byte swizzle inside each 1 KB
 // block (row r, piece p at unit 4 r + ((p + r / 4) & 3)), so that the 16
 // lanes of a group reading one 16-byte operand piece each cover all banks.
 template <int D, int DV, int KVT, bool PVS, int NT, int NK, int NSET>
