@@ -82,11 +82,21 @@ class HipEvent:
             HipEvent._hip.hipEventDestroy(self.ev)
 
 
-# Kernel sources whose text decides the split partial's memory traffic.
-PARTIAL_SOURCES = ("paged_split_kv_append_amd/csrc/partial_mfma.hip",
-                   "paged_split_kv_append_amd/csrc/mfma_common.h",
-                   "paged_split_kv_append_amd/csrc/device_common.h",
-                   "paged_split_kv_append_amd/csrc/partial_valu.hip")
+# Kernel sources whose text decides the split partial's memory traffic: the
+# headers every matrix-core partial includes, and the file of the kernel that
+# serves the shape (multi-row for more than 16 rows per KV head).
+_CSRC = "paged_split_kv_append_amd/csrc/"
+_COMMON_SOURCES = (_CSRC + "partial_common.h", _CSRC + "mfma_common.h", _CSRC + "device_common.h")
+
+
+def partial_sources(workload: int):
+    from paged_split_kv_append_amd import synth
+    cfg = synth.WORKLOADS[workload]
+    if cfg["kv_dtype"] == synth.F32:
+        return (_CSRC + "partial_valu.hip", _CSRC + "device_common.h")
+    rows = cfg["q_heads"] // cfg["kv_heads"] * cfg["q_rows"]
+    kernel = "partial_multirow.hip" if rows > 16 else "partial_mfma.hip"
+    return (_CSRC + kernel,) + _COMMON_SOURCES
 
 
 def _code_only(text: str) -> str:
@@ -98,10 +108,10 @@ def _code_only(text: str) -> str:
     return " ".join(text.split())
 
 
-def partial_source_hash() -> str:
+def partial_source_hash(workload: int) -> str:
     import hashlib
     h = hashlib.sha256()
-    for rel in PARTIAL_SOURCES:
+    for rel in partial_sources(workload):
         with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
             h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
@@ -124,7 +134,7 @@ def load_traffic(workload: int, fused: bool):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("partial_source_sha256_16") != partial_source_hash():
+    if kv.get("partial_source_sha256_16") != partial_source_hash(workload):
         return None
     return int(kv["traffic_bytes_per_launch"])
 
@@ -181,7 +191,7 @@ def summarize_counters(fetch_dir: str, write_dir: str, copy_mib: int, workload: 
         f"fetch_bytes_per_launch: {int(fetch_b)}",
         f"write_bytes_per_launch: {int(write_b)}",
         f"traffic_bytes_per_launch: {int(fetch_b + write_b)}",
-        f"partial_source_sha256_16: {partial_source_hash()}",
+        f"partial_source_sha256_16: {partial_source_hash(workload)}",
     ]
     return "\n".join(lines)
 

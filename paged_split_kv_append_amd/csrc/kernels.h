@@ -137,7 +137,10 @@ struct BoundsArgs {
 };
 hipError_t launch_kv_bounds(const BoundsArgs &a, hipStream_t stream);
 hipError_t launch_partial_valu(const PartialArgs &a, hipStream_t stream);
+// matrix-core partials (bf16 / fp8 pools, bf16 Q): more than 16 rows per KV
+// head go to launch_partial_multirow
 hipError_t launch_partial_mfma(const PartialArgs &a, hipStream_t stream);
+hipError_t launch_partial_multirow(const PartialArgs &a, hipStream_t stream);
 // true when launch_partial_mfma runs `a` as one persistent launch, so that it
 // can also perform the append of a.new_k / a.new_v
 bool partial_mfma_is_persistent(const PartialArgs &a);

@@ -1,0 +1,209 @@
+// Device helpers shared by the split-partial kernels on the matrix cores
+// (the decode kernels of partial_mfma.hip and the multi-row kernel of
+// partial_multirow.hip): sequence length and page lookups, the transposed
+// read of a V operand from LDS, the online-softmax step and the fixed-shift
+// softmax.
+#pragma once
+
+#include "kernels.h"
+#include "mfma_common.h"
+
+namespace nbx {
+
+__device__ __forceinline__ int clamp_len(const PartialArgs &a, int b, bool flag_it)
+{
+    int L = a.seq_lens[b];
+    const int cap = a.max_pages * a.page_tokens;
+    if (L < 0 || L > cap) {
+        if (flag_it)
+            flag_error(a.dev_err, NBX_DEVERR_SEQ_RANGE);
+        L = L < 0 ? 0 : cap;
+    }
+    return L;
+}
+
+// Page of the 16-position tile starting at position ts of sequence b, or -1
+// if the tile is past `end` or the block table does not map it into the pool.
+__device__ __forceinline__ int tile_page(const PartialArgs &a, int b, int ts, int end,
+                                         bool flag_it)
+{
+    if (ts >= end)
+        return -1;
+    const int page = a.block_table[(int64_t)b * a.max_pages + ts / a.page_tokens];
+    if (page < 0 || page >= a.num_pages) {
+        if (flag_it)
+            flag_error(a.dev_err, NBX_DEVERR_PAGE_RANGE);
+        return -1;
+    }
+    return page;
+}
+
+// A operand of the P V product for 16-column slice dt from a column-blocked
+// chunk tile (tile 0 blocks, then tile 1 blocks); `lane_base` is the lane's
+// fixed address: block 0 of tile 0 + (4 g + j/4) * 32 + (j % 4) * 8.
+template <int DT>
+__device__ __forceinline__ u32x4 vt_operand(const uint8_t *lane_base, int dt)
+{
+    const uint8_t *p0 = lane_base + dt * 512;
+    const uint8_t *p1 = p0 + DT * 512;
+    const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4 *)(__attribute__((address_space(3))) uint8_t *)p0);
+    const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4 *)(__attribute__((address_space(3))) uint8_t *)p1);
+    const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+    return u32x4{ua[0], ua[1], ub[0], ub[1]};
+}
+
+// Online-softmax step for one lane's row over NK k-steps of 32 positions (two
+// 16-position tiles each): sc holds the scaled scores (log2 units, -inf where
+// masked).  Updates m, l, rescales o and returns the P operands of the k-steps
+// (hi and residual lo parts).
+template <int DT, bool PVS, int NK>
+__device__ __forceinline__ void softmax_step_n(float (&sc)[2 * NK][4], float &m_run, float &l_run,
+                                               f32x4 (&o)[DT], u32x4 (&ph)[NK], u32x4 (&pl)[NK])
+{
+    float mx = sc[0][0];
+#pragma unroll
+    for (int t = 0; t < 2 * NK; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            mx = fmaxf(mx, sc[t][i]);
+    mx = xor_max16_32(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_safe = m_new == -INFINITY ? 0.0f : m_new;
+    const float corr = fast_exp2(m_run - m_safe);
+    float p[2 * NK][4], psum = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 2 * NK; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[t][i] = fast_exp2(sc[t][i] - m_safe);
+            psum += p[t][i];
+        }
+    l_run = l_run * corr + psum;
+    m_run = m_new;
+    if (__any(corr != 1.0f)) {             // a row's max moved: rescale (else o * 1 = o)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+            o[dt] *= corr;
+    }
+#pragma unroll
+    for (int k = 0; k < NK; ++k)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int t = 2 * k + u;
+            ph[k][2 * u] = pack_bf16(p[t][0], p[t][1]);
+            ph[k][2 * u + 1] = pack_bf16(p[t][2], p[t][3]);
+            if constexpr (PVS) {
+                pl[k][2 * u] =
+                    pack_bf16(p[t][0] - bf16_round(p[t][0]), p[t][1] - bf16_round(p[t][1]));
+                pl[k][2 * u + 1] =
+                    pack_bf16(p[t][2] - bf16_round(p[t][2]), p[t][3] - bf16_round(p[t][3]));
+            }
+        }
+}
+
+// ------------------------------------------------------------------ fixed shift
+//
+// The fixed-shift softmax of the maxdiffusion PR #477 page (fixed-m splash
+// attention with dynamic bounds), in log2 units: a split whose keys have
+// norms <= kb, whose values (in the accumulator's units) are <= Vmax and
+// whose sequence holds N keys gets C = 127 - ceil(log2 N) - ceil(log2 Vmax)
+// and gate = floor((C + 125) / 2); a query row with norm |q| gets U = |scale|
+// |q| kb (an upper bound of every |score|, here enlarged by 2^-12 to cover
+// the rounding of the norms and of the fp32 dot product) and the shift
+// m = ceil(U) - C.  When ceil(U) <= gate every exponent score - m lies in
+// [-125, C]: no term leaves the normal fp32 range and N terms times Vmax
+// stay below 2^127, so p = 2^(score - m) is summed with no running maximum
+// and no rescaling.  Vmax = max(1, V bound * max(1, v_scale)) covers the
+// accumulator both before and after the V scale is applied.
+
+__device__ __forceinline__ int ceil_log2_count(int n)
+{
+    return n <= 1 ? 0 : 32 - __clz(n - 1);
+}
+
+// C and the gate for N keys and a V bound vb (false: the bound is not finite)
+__device__ __forceinline__ bool fixed_shift_consts(int n, float vb, float v_scale, int &C,
+                                                   int &gate)
+{
+    float vmax = vb * fmaxf(1.0f, v_scale);
+    if (!(vmax <= 3.0e38f))                    // NaN (unknown) or infinite
+        return false;
+    vmax = fmaxf(vmax, 1.0f);
+    int e;
+    const float f = frexpf(vmax, &e);          // vmax = f 2^e, f in [0.5, 1)
+    C = 127 - ceil_log2_count(n) - (f == 0.5f ? e - 1 : e);
+    const int W = C + 125;
+    gate = W >= 0 ? W / 2 : -((1 - W) / 2);    // floor(W / 2)
+    return true;
+}
+
+// The row's shift m (log2 units); true when the row passes the gate
+__device__ __forceinline__ bool fixed_shift_row(float q_norm, float kb, float scale_abs, int C,
+                                                int gate, float &m)
+{
+    const float U = scale_abs * q_norm * kb * (1.0f + 0x1p-12f);
+    const float cu = ceilf(U);
+    m = cu - (float)C;
+    return cu <= (float)gate;                  // false for NaN or infinite U
+}
+
+// Norm of this lane's query row from its bf16 operand registers (lane
+// 16 g + j holds columns 8 g .. 8 g + 7 of every 32-column k-step of row j)
+template <int KK>
+__device__ __forceinline__ float q_row_norm(const u32x4 (&qb)[KK])
+{
+    float ss = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float lo = __uint_as_float(qb[kk][w] << 16);
+            const float hi = __uint_as_float(qb[kk][w] & 0xFFFF0000u);
+            ss = fmaf(lo, lo, ss);
+            ss = fmaf(hi, hi, ss);
+        }
+    return sqrtf(xor_sum16_32(ss));
+}
+
+// Softmax step with a fixed shift m: p = 2^(s - m), l += sum p, no rescaling
+// (the P operands as softmax_step_n forms them)
+template <bool PVS, int NK>
+__device__ __forceinline__ void softmax_fixed_n(float (&sc)[2 * NK][4], float m, float &l_run,
+                                                u32x4 (&ph)[NK], u32x4 (&pl)[NK])
+{
+    float p[2 * NK][4], psum = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 2 * NK; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[t][i] = fast_exp2(sc[t][i] - m);
+            psum += p[t][i];
+        }
+    l_run += psum;
+#pragma unroll
+    for (int k = 0; k < NK; ++k)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int t = 2 * k + u;
+            ph[k][2 * u] = pack_bf16(p[t][0], p[t][1]);
+            ph[k][2 * u + 1] = pack_bf16(p[t][2], p[t][3]);
+            if constexpr (PVS) {
+                pl[k][2 * u] =
+                    pack_bf16(p[t][0] - bf16_round(p[t][0]), p[t][1] - bf16_round(p[t][1]));
+                pl[k][2 * u + 1] =
+                    pack_bf16(p[t][2] - bf16_round(p[t][2]), p[t][3] - bf16_round(p[t][3]));
+            }
+        }
+}
+
+// m_part of a row: the fixed shift (no key: -inf) or the running maximum
+__device__ __forceinline__ float stored_m(bool fixed, float m_fix, float m_run, float l_total)
+{
+    if (fixed)
+        return l_total > 0.0f ? m_fix * kLn2 : -INFINITY;
+    return m_run == -INFINITY ? -INFINITY : m_run * kLn2;
+}
+
+}  // namespace nbx

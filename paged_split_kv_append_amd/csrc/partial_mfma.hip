@@ -36,7 +36,8 @@
 // constant offset from one per-lane address.  Page ids come from the block
 // table once per 32 chunks (one per lane) and are broadcast with readlane.
 //
-// Three kernels:
+// Two kernels here (the multi-row kernel, which shares the products, operand
+// layouts and softmax, is in partial_multirow.hip):
 //  - decode_persistent_kernel: at most 16 rows per KV head (decode, short
 //    windows) and at most 256 sequences; one wave per (sequence, split, KV
 //    head) item, as many waves as the device holds, items enumerated on the
@@ -44,58 +45,20 @@
 //  - decode_mfma_kernel: the same rows for larger batches.  PG waves per
 //    (split, sequence x KV head) take interleaved chunks of the split, each
 //    with its own (m, l, O), combined in a fixed order at the end.
-//    In both decode kernels K rows go from HBM straight into MFMA operand
-//    registers; V rows are loaded into registers and written to the wave's
-//    LDS tile once they land (fp8 codes widened on the way).  The wave's next
-//    chunk is loaded while the current one is computed.
-//  - multirow_mfma_kernel: more rows per KV head (verify windows, prompt
-//    chunks).  A workgroup takes RW x NT row tiles of 16 rows; its waves share
-//    the loads of each K and V chunk and stage it in LDS (K column-blocked by
-//    64 bytes, which makes the operand reads conflict-free too); the next
-//    chunk is in registers while the current one is computed.
-//    Workgroups are ordered row block fastest and mapped so that the row
-//    blocks of one split run on the same XCD and share its L2 (the rows-first
-//    order of TensorFold PR #1219, made XCD-aware).
-// The persistent and multi-row kernels also take the fixed-shift softmax
-// when both pools carry per-page bounds (see "fixed shift" below).
+// In both, K rows go from HBM straight into MFMA operand registers; V rows
+// are loaded into registers and written to the wave's LDS tile once they land
+// (fp8 codes widened on the way).  The wave's next chunk is loaded while the
+// current one is computed.  The persistent kernel also takes the fixed-shift
+// softmax (partial_common.h) when both pools carry per-page bounds.
 #include <atomic>
 
-#include "kernels.h"
-#include "mfma_common.h"
+#include "partial_common.h"
 
 namespace nbx {
 
 namespace {
 
 constexpr int kChunk = 32;   // positions per chunk: two 16-position tiles, one PV k-step
-
-__device__ __forceinline__ int clamp_len(const PartialArgs &a, int b, bool flag_it)
-{
-    int L = a.seq_lens[b];
-    const int cap = a.max_pages * a.page_tokens;
-    if (L < 0 || L > cap) {
-        if (flag_it)
-            flag_error(a.dev_err, NBX_DEVERR_SEQ_RANGE);
-        L = L < 0 ? 0 : cap;
-    }
-    return L;
-}
-
-// Page of the 16-position tile starting at position ts of sequence b, or -1
-// if the tile is past `end` or the block table does not map it into the pool.
-__device__ __forceinline__ int tile_page(const PartialArgs &a, int b, int ts, int end,
-                                         bool flag_it)
-{
-    if (ts >= end)
-        return -1;
-    const int page = a.block_table[(int64_t)b * a.max_pages + ts / a.page_tokens];
-    if (page < 0 || page >= a.num_pages) {
-        if (flag_it)
-            flag_error(a.dev_err, NBX_DEVERR_PAGE_RANGE);
-        return -1;
-    }
-    return page;
-}
 
 // Lane i of the result: page of tile (i & 1) of chunk c0 + (i / 2) * cstep,
 // -1 past the split.  Refreshed once per 32 chunks of a wave.
@@ -122,71 +85,6 @@ __device__ __forceinline__ i32x4 tile_rsrc(const void *data, int64_t stride_page
     return make_buffer_rsrc(base, bytes);
 }
 
-// A operand of the P V product for 16-column slice dt from a column-blocked
-// chunk tile (tile 0 blocks, then tile 1 blocks); `lane_base` is the lane's
-// fixed address: block 0 of tile 0 + (4 g + j/4) * 32 + (j % 4) * 8.
-template <int DT>
-__device__ __forceinline__ u32x4 vt_operand(const uint8_t *lane_base, int dt)
-{
-    const uint8_t *p0 = lane_base + dt * 512;
-    const uint8_t *p1 = p0 + DT * 512;
-    const bf16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (lds_bf16x4 *)(__attribute__((address_space(3))) uint8_t *)p0);
-    const bf16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-        (lds_bf16x4 *)(__attribute__((address_space(3))) uint8_t *)p1);
-    const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
-    return u32x4{ua[0], ua[1], ub[0], ub[1]};
-}
-
-// Online-softmax step for one lane's row over NK k-steps of 32 positions (two
-// 16-position tiles each): sc holds the scaled scores (log2 units, -inf where
-// masked).  Updates m, l, rescales o and returns the P operands of the k-steps
-// (hi and residual lo parts).
-template <int DT, bool PVS, int NK>
-__device__ __forceinline__ void softmax_step_n(float (&sc)[2 * NK][4], float &m_run, float &l_run,
-                                               f32x4 (&o)[DT], u32x4 (&ph)[NK], u32x4 (&pl)[NK])
-{
-    float mx = sc[0][0];
-#pragma unroll
-    for (int t = 0; t < 2 * NK; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            mx = fmaxf(mx, sc[t][i]);
-    mx = xor_max16_32(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_safe = m_new == -INFINITY ? 0.0f : m_new;
-    const float corr = fast_exp2(m_run - m_safe);
-    float p[2 * NK][4], psum = 0.0f;
-#pragma unroll
-    for (int t = 0; t < 2 * NK; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            p[t][i] = fast_exp2(sc[t][i] - m_safe);
-            psum += p[t][i];
-        }
-    l_run = l_run * corr + psum;
-    m_run = m_new;
-    if (__any(corr != 1.0f)) {             // a row's max moved: rescale (else o * 1 = o)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-            o[dt] *= corr;
-    }
-#pragma unroll
-    for (int k = 0; k < NK; ++k)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int t = 2 * k + u;
-            ph[k][2 * u] = pack_bf16(p[t][0], p[t][1]);
-            ph[k][2 * u + 1] = pack_bf16(p[t][2], p[t][3]);
-            if constexpr (PVS) {
-                pl[k][2 * u] =
-                    pack_bf16(p[t][0] - bf16_round(p[t][0]), p[t][1] - bf16_round(p[t][1]));
-                pl[k][2 * u + 1] =
-                    pack_bf16(p[t][2] - bf16_round(p[t][2]), p[t][3] - bf16_round(p[t][3]));
-            }
-        }
-}
-
 // Online-softmax step for one lane's row over the 32 positions of a chunk
 // (softmax_step_n with one k-step): returns the P operand (hi and residual lo).
 template <int DT, bool PVS>
@@ -197,109 +95,6 @@ __device__ __forceinline__ void softmax_step(float (&sc)[2][4], float &m_run, fl
     softmax_step_n<DT, PVS, 1>(sc, m_run, l_run, o, ph1, pl1);
     ph = ph1[0];
     pl = pl1[0];
-}
-
-// ------------------------------------------------------------------ fixed shift
-//
-// The fixed-shift softmax of the maxdiffusion PR #477 page (fixed-m splash
-// attention with dynamic bounds), in log2 units: a split whose keys have
-// norms <= kb, whose values (in the accumulator's units) are <= Vmax and
-// whose sequence holds N keys gets C = 127 - ceil(log2 N) - ceil(log2 Vmax)
-// and gate = floor((C + 125) / 2); a query row with norm |q| gets U = |scale|
-// |q| kb (an upper bound of every |score|, here enlarged by 2^-12 to cover
-// the rounding of the norms and of the fp32 dot product) and the shift
-// m = ceil(U) - C.  When ceil(U) <= gate every exponent score - m lies in
-// [-125, C]: no term leaves the normal fp32 range and N terms times Vmax
-// stay below 2^127, so p = 2^(score - m) is summed with no running maximum
-// and no rescaling.  Vmax = max(1, V bound * max(1, v_scale)) covers the
-// accumulator both before and after the V scale is applied.
-
-__device__ __forceinline__ int ceil_log2_count(int n)
-{
-    return n <= 1 ? 0 : 32 - __clz(n - 1);
-}
-
-// C and the gate for N keys and a V bound vb (false: the bound is not finite)
-__device__ __forceinline__ bool fixed_shift_consts(int n, float vb, float v_scale, int &C,
-                                                   int &gate)
-{
-    float vmax = vb * fmaxf(1.0f, v_scale);
-    if (!(vmax <= 3.0e38f))                    // NaN (unknown) or infinite
-        return false;
-    vmax = fmaxf(vmax, 1.0f);
-    int e;
-    const float f = frexpf(vmax, &e);          // vmax = f 2^e, f in [0.5, 1)
-    C = 127 - ceil_log2_count(n) - (f == 0.5f ? e - 1 : e);
-    const int W = C + 125;
-    gate = W >= 0 ? W / 2 : -((1 - W) / 2);    // floor(W / 2)
-    return true;
-}
-
-// The row's shift m (log2 units); true when the row passes the gate
-__device__ __forceinline__ bool fixed_shift_row(float q_norm, float kb, float scale_abs, int C,
-                                                int gate, float &m)
-{
-    const float U = scale_abs * q_norm * kb * (1.0f + 0x1p-12f);
-    const float cu = ceilf(U);
-    m = cu - (float)C;
-    return cu <= (float)gate;                  // false for NaN or infinite U
-}
-
-// Norm of this lane's query row from its bf16 operand registers (lane
-// 16 g + j holds columns 8 g .. 8 g + 7 of every 32-column k-step of row j)
-template <int KK>
-__device__ __forceinline__ float q_row_norm(const u32x4 (&qb)[KK])
-{
-    float ss = 0.0f;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float lo = __uint_as_float(qb[kk][w] << 16);
-            const float hi = __uint_as_float(qb[kk][w] & 0xFFFF0000u);
-            ss = fmaf(lo, lo, ss);
-            ss = fmaf(hi, hi, ss);
-        }
-    return sqrtf(xor_sum16_32(ss));
-}
-
-// Softmax step with a fixed shift m: p = 2^(s - m), l += sum p, no rescaling
-// (the P operands as softmax_step_n forms them)
-template <bool PVS, int NK>
-__device__ __forceinline__ void softmax_fixed_n(float (&sc)[2 * NK][4], float m, float &l_run,
-                                                u32x4 (&ph)[NK], u32x4 (&pl)[NK])
-{
-    float p[2 * NK][4], psum = 0.0f;
-#pragma unroll
-    for (int t = 0; t < 2 * NK; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            p[t][i] = fast_exp2(sc[t][i] - m);
-            psum += p[t][i];
-        }
-    l_run += psum;
-#pragma unroll
-    for (int k = 0; k < NK; ++k)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int t = 2 * k + u;
-            ph[k][2 * u] = pack_bf16(p[t][0], p[t][1]);
-            ph[k][2 * u + 1] = pack_bf16(p[t][2], p[t][3]);
-            if constexpr (PVS) {
-                pl[k][2 * u] =
-                    pack_bf16(p[t][0] - bf16_round(p[t][0]), p[t][1] - bf16_round(p[t][1]));
-                pl[k][2 * u + 1] =
-                    pack_bf16(p[t][2] - bf16_round(p[t][2]), p[t][3] - bf16_round(p[t][3]));
-            }
-        }
-}
-
-// m_part of a row: the fixed shift (no key: -inf) or the running maximum
-__device__ __forceinline__ float stored_m(bool fixed, float m_fix, float m_run, float l_total)
-{
-    if (fixed)
-        return l_total > 0.0f ? m_fix * kLn2 : -INFINITY;
-    return m_run == -INFINITY ? -INFINITY : m_run * kLn2;
 }
 
 // ------------------------------------------------------------------ decode
@@ -948,331 +743,7 @@ decode_persistent_kernel(PartialArgs a)
             break;
     }
 }
-
-// ------------------------------------------------------------------ multi-row
-
-// A workgroup of 8 waves takes 8 x NT row tiles of 16 rows of one (sequence,
-// KV head, split).  The K and V tiles of a chunk are pieces of 1 KB (as bf16:
-// 16 rows x 32 columns); waves 0-3 load the K pieces and waves 4-7 the V
-// pieces, each wave all its pieces from one tile, so each of its loads has a
-// fixed role (K or V, tile) and one descriptor per tile serves it.  Chunk c + 1
-// waits in LDS and chunks c + 2 ... c + 1 + NSET in registers while chunk c is
-// computed; one barrier per chunk.  K is stored in LDS with a 16-byte swizzle inside each 1 KB
-// block (row r, piece p at unit 4 r + ((p + r / 4) & 3)), so that the 16
-// lanes of a group reading one 16-byte operand piece each cover all banks.
-template <int D, int DV, int KVT, bool PVS, int NT, int NK, int NSET>
-__global__ void __launch_bounds__(512)
-multirow_mfma_kernel(PartialArgs a, int row_blocks)
-{
-    constexpr int RW = 8;                      // waves per workgroup
-    constexpr int CH = 32 * NK;                // positions per chunk (NK k-steps of P V)
-    constexpr int TL = 2 * NK;                 // 16-position tiles per chunk
-    constexpr int BATCH = 64 / TL;             // chunks whose tiles fill one lane register
-    constexpr int KK = D / 32, DT = DV / 16;
-    constexpr int KV = DV / 32;                // 32-column V pieces per tile
-    constexpr bool BF = KVT == NBX_BF16;
-    constexpr int ESZ = BF ? 2 : 1;
-    constexpr int KBYTES = CH * 2 * D;         // K chunk as bf16: [tile][KK][16 rows][64 B]
-    constexpr int VBYTES = CH * 2 * DV;        // V chunk as bf16: [tile][DT][16 rows][32 B]
-    constexpr int BUF = KBYTES + VBYTES;
-    // pieces per wave: TL x KK of K over waves 0-3, TL x KV of V over waves 4-7
-    constexpr int PER_K = TL * KK / 4, PER_V = TL * KV / 4;
-    constexpr int PMAX = PER_K > PER_V ? PER_K : PER_V;
-    static_assert(PER_K <= KK && KK % PER_K == 0 && PER_V <= KV && KV % PER_V == 0,
-                  "a wave's pieces lie in one tile");
-    constexpr int R = RW * NT * 16;            // rows per workgroup
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF];
-
-    const uint32_t id = xcd_contiguous_id(blockIdx.x, gridDim.x);
-    const int rb = (int)(id % (uint32_t)row_blocks);
-    const int rest = (int)(id / (uint32_t)row_blocks);
-    const int s = rest % a.n_split;
-    const int bg = rest / a.n_split;
-    const int b = bg / a.kv_heads, gk = bg % a.kv_heads;
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index, uniform
-    const int g = lane >> 4, j = lane & 15;
-    const int M = a.rows_per_kv;
-    const int row_lo = rb * R, row_hi = min(M, row_lo + R);
-    const int64_t row_base = ((int64_t)b * a.q_heads + (int64_t)gk * a.group) * a.q_rows;
-    const bool lead = threadIdx.x == 0;
-    // a wave whose row tiles are all past the last row loads its share only
-    const bool has_rows = row_lo + w * NT * 16 < row_hi;
-
-    const int S = device_split_size(a);
-    const int L = clamp_len(a, b, lead && s == 0 && rb == 0);
-    if (lead && rb == 0 && s == a.n_split - 1 && L > a.n_split * S)
-        flag_error(a.dev_err, NBX_DEVERR_SEQ_RANGE);
-
-    const int wb = seq_window(a, b, lead && s == 0 && rb == 0);
-    int n_row[NT];
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-        const int m = row_lo + (w * NT + n) * 16 + j;
-        n_row[n] = m < row_hi ? row_keys(a, L, wb, m % a.q_rows) : 0;
-    }
-    int n_max = 0;                             // the most keys a row of this block sees
-    for (int m = row_lo; m < row_hi && m < row_lo + a.q_rows; ++m)
-        n_max = max(n_max, row_keys(a, L, wb, m % a.q_rows));
-    const int j0 = s * S;
-    const int jend = min(j0 + S, n_max);
-    const int nchunk = jend > j0 ? (jend - j0 + CH - 1) / CH : 0;
-
-    u32x4 qb[NT][KK];
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-        const int m = row_lo + (w * NT + n) * 16 + j;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-            qb[n][kk] = m < row_hi ? *(const u32x4 *)((const uint16_t *)a.q + (row_base + m) * D +
-                                                      kk * 32 + g * 8)
-                                   : u32x4{0, 0, 0, 0};
-    }
-    const float scale2 = a.scale * a.k_scale * kLog2e;
-    float m_run[NT], l_run[NT];
-    f32x4 o[NT][DT];
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-        m_run[n] = -INFINITY;
-        l_run[n] = 0.0f;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-            o[n][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-    // fixed-shift softmax where both pools carry bounds: per row tile, a shift
-    // per row and one decision for the tile's 16 rows
-    bool fixed[NT];
-    float m_fix[NT];
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-        fixed[n] = false;
-        m_fix[n] = 0.0f;
-    }
-    if (a.k_bounds != nullptr && a.v_bounds != nullptr && nchunk > 0) {
-        float kb = 0.0f, vb = 0.0f;
-        const int T = a.page_tokens;
-        for (int pi = j0 / T + lane; pi <= (jend - 1) / T; pi += 64) {
-            const int page = a.block_table[(int64_t)b * a.max_pages + pi];
-            if (page >= 0 && page < a.num_pages) {
-                kb = bound_max(kb, a.k_bounds[(int64_t)page * a.kv_heads + gk]);
-                vb = bound_max(vb, a.v_bounds[(int64_t)page * a.kv_heads + gk]);
-            }
-        }
-        kb = group_bound_max<64>(kb);
-        vb = group_bound_max<64>(vb);
-        int C, gate;
-        if (fixed_shift_consts(L, vb, a.v_scale, C, gate)) {
-#pragma unroll
-            for (int n = 0; n < NT; ++n)
-                fixed[n] = __all(fixed_shift_row(q_row_norm<KK>(qb[n]), kb, fabsf(scale2), C, gate,
-                                                 m_fix[n]));
-        }
-    }
-
-    const int64_t k_head = (int64_t)gk * a.k_stride_head;
-    const int64_t v_head = (int64_t)gk * a.v_stride_head;
-    const int kst_b = (int)(a.k_stride_token * ESZ), vst_b = (int)(a.v_stride_token * ESZ);
-    // fixed per-lane byte offsets of the 64-lane piece loads
-    const int k_lane = (lane >> 2) * kst_b + (lane & 3) * 8 * ESZ;   // + kk * 32 * ESZ
-    const int v_lane = ((lane & 31) >> 1) * vst_b + ((lane >> 5) * 16 + (lane & 1) * 8) * ESZ;
-    // LDS: swizzled K store of this lane (row lane / 4, piece lane % 4) and
-    // read of operand piece g of row j; transposed V read
-    const int k_st = (4 * (lane >> 2) + (((lane & 3) + (lane >> 4)) & 3)) * 16;
-    const uint8_t *k_rd = smem + (4 * j + ((g + (j >> 2)) & 3)) * 16;   // + (t*KK + kk) * 1024
-    const uint8_t *vt_lane = smem + KBYTES + (4 * g + (j >> 2)) * 32 + (j & 3) * 8;
-
-    // Wave roles: waves 0-3 load K, 4-7 load V; of the pieces of its pool
-    // (tile-major: K 32-column groups kk, V 32-column pairs of 16-column
-    // slices) wave w takes (w & 3) * per ... (w & 3) * per + per - 1, all in
-    // tile t_w of every chunk.
-    const bool is_k = w < 4;
-    const int per = is_k ? PER_K : PER_V, pieces = is_k ? KK : KV;
-    const int t_w = ((w & 3) * per) / pieces, pbase = ((w & 3) * per) % pieces;
-    const uint8_t *role_base = is_k ? (const uint8_t *)a.k_data + k_head * ESZ
-                                    : (const uint8_t *)a.v_data + v_head * ESZ;
-    const int64_t role_sp = (is_k ? a.k_stride_page : a.v_stride_page) * ESZ;
-    const int role_st = is_k ? kst_b : vst_b;
-    const int role_lane = (is_k ? k_lane : v_lane) + pbase * 32 * ESZ;
-
-    // Tiles of the chunks of even / odd batches of BATCH chunks, lane i holding
-    // tile i % TL of chunk BATCH batch + i / TL: the byte offset of its first row from
-    // this wave's pool and head (lo, hi), the bytes this wave may read from it
-    // (0 for a tile outside the sequence or the pool) and whether it is mapped
-    // (K bytes).  Two sets, so that refreshing the next batch keeps the tiles
-    // of chunks still in flight; filled once per batch.
-    uint32_t off_lo0 = 0, off_hi0 = 0, nbytes0 = 0, kvalid0 = 0;     // even batches
-    uint32_t off_lo1 = 0, off_hi1 = 0, nbytes1 = 0, kvalid1 = 0;     // odd batches
-    auto refresh = [&](int c) {
-        const int cq = c + lane / TL;
-        const int ts = j0 + cq * CH + 16 * (lane % TL);
-        const int page = cq < nchunk ? tile_page(a, b, ts, jend, lead) : -1;
-        const int row = ts % a.page_tokens;
-        const bool ok = page >= 0;
-        const int64_t off = ok ? (int64_t)page * role_sp + (int64_t)row * role_st : 0;
-        const int vrows = min(16, max(jend - ts, 0));
-        const uint32_t lo = (uint32_t)off, hi = (uint32_t)((uint64_t)off >> 32);
-        const uint32_t nb = ok ? (uint32_t)((is_k ? 16 : vrows) * role_st) : 0u;
-        if ((c / BATCH) & 1) {
-            off_lo1 = lo;
-            off_hi1 = hi;
-            nbytes1 = nb;
-            kvalid1 = ok;
-        } else {
-            off_lo0 = lo;
-            off_hi0 = hi;
-            nbytes0 = nb;
-            kvalid0 = ok;
-        }
-    };
-    auto tile_ok = [&](int c, int t) {
-        const uint32_t r = ((c / BATCH) & 1) ? kvalid1 : kvalid0;
-        return __builtin_amdgcn_readlane(r, TL * (c % BATCH) + t) != 0;
-    };
-
-    struct Regs {
-        u32x4 r16[BF ? PMAX : 1];
-        u32x2 r8[BF ? 1 : PMAX];
-    };
-    // this wave's pieces of chunk c into registers: one descriptor per chunk
-    auto issue = [&](int c, Regs &rg) {
-        const int q = (c / BATCH) & 1, li = TL * (c % BATCH) + t_w;
-        const uint32_t lo = __builtin_amdgcn_readlane(q ? off_lo1 : off_lo0, li);
-        const uint32_t hi = __builtin_amdgcn_readlane(q ? off_hi1 : off_hi0, li);
-        const uint32_t nb = __builtin_amdgcn_readlane(q ? nbytes1 : nbytes0, li);
-        const i32x4 rs = make_buffer_rsrc(role_base + (((uint64_t)hi << 32) | lo), nb);
-#pragma unroll
-        for (int x = 0; x < PMAX; ++x) {
-            if (x >= per)                      // (never taken when K and V widths match)
-                break;
-            if constexpr (BF)
-                rg.r16[x] = nbx_buffer_load_b128(rs, role_lane + x * 32 * ESZ, 0, 0);
-            else
-                rg.r8[x] = nbx_buffer_load_b64(rs, role_lane + x * 32 * ESZ, 0, 0);
-        }
-    };
-    // this wave's pieces of a chunk, landed in registers, into an LDS buffer
-    // (rows outside a descriptor range were read as zeros)
-    auto land = [&](uint8_t *buf, const Regs &rg) {
-        uint8_t *dst = is_k ? buf + (t_w * KK + pbase) * 1024 + k_st
-                            : buf + KBYTES + t_w * DT * 512 + pbase * 1024 + lane * 16;
-#pragma unroll
-        for (int x = 0; x < PMAX; ++x) {
-            if (x >= per)
-                break;
-            if constexpr (BF)
-                *(u32x4 *)(dst + x * 1024) = rg.r16[x];
-            else
-                *(u32x4 *)(dst + x * 1024) = widen8_e4m3(rg.r8[x]);
-        }
-    };
-    auto compute = [&](int c, int boff) {
-        const int p0 = j0 + c * CH;
-        bool ok[TL];
-#pragma unroll
-        for (int t = 0; t < TL; ++t)
-            ok[t] = tile_ok(c, t);
-        f32x4 acc[NT][TL];
-#pragma unroll
-        for (int n = 0; n < NT; ++n)
-#pragma unroll
-            for (int t = 0; t < TL; ++t)
-                acc[n][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-            for (int t = 0; t < TL; ++t) {
-                const u32x4 ka = *(const u32x4 *)(k_rd + boff + (t * KK + kk) * 1024);
-#pragma unroll
-                for (int n = 0; n < NT; ++n)
-                    acc[n][t] = mfma_bf16(ka, qb[n][kk], acc[n][t]);
-            }
-        u32x4 ph[NT][NK], pl[NT][NK];
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-            const int e_n = min(jend, n_row[n]);
-            float sc[TL][4];
-#pragma unroll
-            for (int t = 0; t < TL; ++t) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int pos = p0 + 16 * t + 4 * g + i;
-                    sc[t][i] = (ok[t] && pos < e_n) ? acc[n][t][i] * scale2 : -INFINITY;
-                }
-            }
-            if (fixed[n])
-                softmax_fixed_n<PVS, NK>(sc, m_fix[n], l_run[n], ph[n], pl[n]);
-            else
-                softmax_step_n<DT, PVS, NK>(sc, m_run[n], l_run[n], o[n], ph[n], pl[n]);
-        }
-#pragma unroll
-        for (int kq = 0; kq < NK; ++kq)
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const u32x4 va = vt_operand<DT>(vt_lane + boff + kq * 2 * DT * 512, dt);
-#pragma unroll
-                for (int n = 0; n < NT; ++n) {
-                    o[n][dt] = mfma_bf16(va, ph[n][kq], o[n][dt]);
-                    if constexpr (PVS)
-                        o[n][dt] = mfma_bf16(va, pl[n][kq], o[n][dt]);
-                }
-            }
-    };
-
-    // Iteration c: barrier (chunk c is in LDS buffer c & 1, every wave is done
-    // with chunk c - 1), compute chunk c, land chunk c + 1 from registers into
-    // buffer (c + 1) & 1, issue chunk c + 1 + NSET into the registers just
-    // freed (NSET register sets: NSET + 1 chunks ahead of the one computed).
-    // Loads and landings past the last chunk are issued all the same (their
-    // descriptors are empty, so they read zeros and touch no memory): with no
-    // branch around them the waits for each register set stay exact and the
-    // chunks behind it stay in flight.
-    Regs rset[NSET];
-    auto step = [&](int c, Regs &land_regs) {
-        __syncthreads();
-        if (has_rows && c < nchunk)
-            compute(c, (c & 1) * BUF);
-        land(smem + ((c + 1) & 1) * BUF, land_regs);
-        if ((c + 1 + NSET) % BATCH == 0)
-            refresh(c + 1 + NSET);
-        issue(c + 1 + NSET, land_regs);
-    };
-    if (nchunk > 0) {
-        refresh(0);
-        issue(0, rset[0]);
-        land(smem, rset[0]);
-        issue(1, rset[0]);
-        if constexpr (NSET == 2)
-            issue(2, rset[1]);
-        for (int c = 0; c < nchunk; c += NSET) {
-            step(c, rset[0]);                  // lands c + 1, reissues c + 1 + NSET there
-            if constexpr (NSET == 2)
-                step(c + 1, rset[1]);          // lands c + 2, reissues c + 4 there
-        }
-    }
-
-    const float vs = a.v_scale;
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-        const float lt = xor_sum16_32(l_run[n]);
-        const int m = row_lo + (w * NT + n) * 16 + j;
-        if (m < row_hi) {
-            const int64_t row = row_base + m;
-            float *op = a.o_part + (row * a.n_split + s) * DV;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-                *(f32x4 *)(op + dt * 16 + 4 * g) = o[n][dt] * vs;
-            if (g == 0) {
-                a.m_part[row * a.n_split + s] = stored_m(fixed[n], m_fix[n], m_run[n], lt);
-                a.l_part[row * a.n_split + s] = lt;
-            }
-        }
-    }
-}
-
 // ------------------------------------------------------------------ dispatch
-
-// multi-row chunks: 2 k-steps (64 positions), one register set in flight
-constexpr int kMrNK = 2, kMrNSet = 1;
 
 
 // Waves the current device holds at once for the persistent decode kernel
@@ -1322,10 +793,11 @@ bool persistent_shape(const PartialArgs &a)
     return a.rows_per_kv <= 16 && a.batch <= kPersistMaxBatch;
 }
 
+// at most 16 rows per KV head: the persistent kernel, else (larger batches)
+// the per-split workgroup kernel
 template <int D, int DV, int KVT, bool PVS>
 hipError_t launch_kind(const PartialArgs &a, hipStream_t stream)
 {
-    const int M = a.rows_per_kv;
     if (persistent_shape(a)) {
         const bool fa = a.new_k != nullptr && a.n_new > 0;
         // bounds matter to the fused append (any pool) and to the reads (both)
@@ -1342,38 +814,20 @@ hipError_t launch_kind(const PartialArgs &a, hipStream_t stream)
     }
     if (a.new_k != nullptr && a.n_new > 0)
         return hipErrorInvalidValue;           // the caller appends first for these shapes
-    if (M <= 16) {
-        // waves per (split, head): enough that each wave's run of chunks is short
-        const int split = a.split_size > 0 ? a.split_size
-                                           : (a.max_pages * a.page_tokens + a.n_split - 1) / a.n_split;
-        const int chunks = (split + kChunk - 1) / kChunk;
-        const int64_t blocks = (int64_t)a.n_split * a.batch * a.kv_heads;
-        if (blocks > 0x7FFFFFFF)
-            return hipErrorInvalidConfiguration;
-        dim3 grid((unsigned)blocks);
-        if (chunks >= 16)
-            hipLaunchKernelGGL((decode_mfma_kernel<D, DV, KVT, PVS, 4>), grid, dim3(256), 0, stream,
-                               a);
-        else if (chunks >= 4)
-            hipLaunchKernelGGL((decode_mfma_kernel<D, DV, KVT, PVS, 2>), grid, dim3(128), 0, stream,
-                               a);
-        else
-            hipLaunchKernelGGL((decode_mfma_kernel<D, DV, KVT, PVS, 1>), grid, dim3(64), 0, stream,
-                               a);
-        return hipGetLastError();
-    }
-    const int64_t heads = (int64_t)a.batch * a.kv_heads * a.n_split;
-    const int nt = multirow_tiles(M, D);
-    const int row_blocks = multirow_row_blocks(M, D);
-    const int64_t blocks = heads * row_blocks;
+    // waves per (split, head): enough that each wave's run of chunks is short
+    const int split = a.split_size > 0 ? a.split_size
+                                       : (a.max_pages * a.page_tokens + a.n_split - 1) / a.n_split;
+    const int chunks = (split + kChunk - 1) / kChunk;
+    const int64_t blocks = (int64_t)a.n_split * a.batch * a.kv_heads;
     if (blocks > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
-    if (nt == 2)
-        hipLaunchKernelGGL((multirow_mfma_kernel<D, DV, KVT, PVS, 2, kMrNK, kMrNSet>),
-                           dim3((unsigned)blocks), dim3(512), 0, stream, a, row_blocks);
+    dim3 grid((unsigned)blocks);
+    if (chunks >= 16)
+        hipLaunchKernelGGL((decode_mfma_kernel<D, DV, KVT, PVS, 4>), grid, dim3(256), 0, stream, a);
+    else if (chunks >= 4)
+        hipLaunchKernelGGL((decode_mfma_kernel<D, DV, KVT, PVS, 2>), grid, dim3(128), 0, stream, a);
     else
-        hipLaunchKernelGGL((multirow_mfma_kernel<D, DV, KVT, PVS, 1, kMrNK, kMrNSet>),
-                           dim3((unsigned)blocks), dim3(512), 0, stream, a, row_blocks);
+        hipLaunchKernelGGL((decode_mfma_kernel<D, DV, KVT, PVS, 1>), grid, dim3(64), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -1392,21 +846,10 @@ hipError_t launch_d(const PartialArgs &a, hipStream_t stream)
 
 bool partial_mfma_is_persistent(const PartialArgs &a) { return persistent_shape(a); }
 
-// 8 waves x 16 rows per multi-row workgroup (8 x 32 where a KV head has more
-// rows than that and D <= 128: D = 256 would spill at 32 rows per wave)
-int multirow_tiles(int rows_per_kv, int head_dim)
-{
-    return rows_per_kv > 128 && head_dim <= 128 ? 2 : 1;
-}
-
-int multirow_row_blocks(int rows_per_kv, int head_dim)
-{
-    const int r = 128 * multirow_tiles(rows_per_kv, head_dim);
-    return (rows_per_kv + r - 1) / r;
-}
-
 hipError_t launch_partial_mfma(const PartialArgs &a, hipStream_t stream)
 {
+    if (a.rows_per_kv > 16)
+        return launch_partial_multirow(a, stream);
     // bf16 pools carry P as hi + lo parts; fp8 pools (tolerance set by their
     // 3-bit mantissa) use the bf16-rounded P alone
     if (a.kv_dtype == NBX_BF16)

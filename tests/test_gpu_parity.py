@@ -149,7 +149,9 @@ def test_merge_matches_oracle_on_oracle_partials(rows, ns, D):
     o64, m64, l64 = (np.float32(x).astype(np.float64) for x in (o, m, l))
     ref = oracle.merge(o64, m64, l64)
     # fp32 sums of ns weighted terms: error within ns * 2^-24 of the absolute sum (x 4)
-    w = np.where(m64 == -np.inf, 0.0, np.exp(m64 - np.max(m64, axis=1, keepdims=True)))
+    top = np.max(m64, axis=1, keepdims=True)
+    top = np.where(top == -np.inf, 0.0, top)          # the empty row: every weight is 0
+    w = np.where(m64 == -np.inf, 0.0, np.exp(m64 - top))
     den = np.maximum((w * l64).sum(1), 1e-300)
     bound = 4 * (ns + 8) * 2.0 ** -24 * ((w[:, :, None] * np.abs(o64)).sum(1) / den[:, None]
                                          + np.abs(ref))
