@@ -115,16 +115,50 @@ __device__ __forceinline__ float fast_exp2(float x)
     return __builtin_amdgcn_exp2f(x);
 }
 
+// Maximum / sum over the four lanes j, j + 16, j + 32, j + 48 (the four
+// lanes holding one row of a 16 x 16 MFMA result), with the gfx950 lane swaps:
+// v_permlane16_swap hands each lane its own value and the one 16 lanes away
+// (lanes 0-15 <-> 16-31, 32-47 <-> 48-63), v_permlane32_swap its own and the
+// one 32 lanes away, on the vector ALU rather than through LDS as a shuffle
+// would.  Both operands of each step are the same pair of values in some order,
+// and max and + are commutative, so the result is that of the xor-16 / xor-32
+// butterfly bit for bit.  All 64 lanes must be active.
+__device__ __forceinline__ float pair16_max(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float pair32_max(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float pair16_sum(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float pair32_sum(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float xor_max16_32(float v)
 {
-    v = fmaxf(v, __shfl_xor(v, 16, 64));
-    return fmaxf(v, __shfl_xor(v, 32, 64));
+    return pair32_max(pair16_max(v));
 }
 
 __device__ __forceinline__ float xor_sum16_32(float v)
 {
-    v += __shfl_xor(v, 16, 64);
-    return v + __shfl_xor(v, 32, 64);
+    return pair32_sum(pair16_sum(v));
 }
 
 // Hardware workgroup id -> logical id such that each of the 8 XCDs (which

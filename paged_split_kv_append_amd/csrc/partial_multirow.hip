@@ -352,12 +352,15 @@ hipError_t launch_mr(const PartialArgs &a, hipStream_t stream)
     const int64_t blocks = heads * row_blocks;
     if (blocks > 0x7FFFFFFF)
         return hipErrorInvalidConfiguration;
-    if (nt == 2)
-        hipLaunchKernelGGL((multirow_mfma_kernel<D, DV, KVT, PVS, 2, kMrNK, kMrNSet>),
-                           dim3((unsigned)blocks), dim3(512), 0, stream, a, row_blocks);
-    else
-        hipLaunchKernelGGL((multirow_mfma_kernel<D, DV, KVT, PVS, 1, kMrNK, kMrNSet>),
-                           dim3((unsigned)blocks), dim3(512), 0, stream, a, row_blocks);
+    if constexpr (D <= 128) {                 // two row tiles per wave only below D = 256
+        if (nt == 2) {
+            hipLaunchKernelGGL((multirow_mfma_kernel<D, DV, KVT, PVS, 2, kMrNK, kMrNSet>),
+                               dim3((unsigned)blocks), dim3(512), 0, stream, a, row_blocks);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((multirow_mfma_kernel<D, DV, KVT, PVS, 1, kMrNK, kMrNSet>),
+                       dim3((unsigned)blocks), dim3(512), 0, stream, a, row_blocks);
     return hipGetLastError();
 }
 
