@@ -111,7 +111,7 @@ typedef struct {
     int32_t page_tokens;    /* a multiple of 16 */
     int32_t head_dim;       /* 64, 128, 192 or 256; a K / V pair of a read is
                                (64, 64), (128, 128), (256, 256) or (192, 128) */
-    int64_t stride_page;    /* elements; stride_token >= head_dim */
+    int64_t stride_page;    /* elements; head_dim <= stride_token <= 2^24 */
     int64_t stride_head;
     int64_t stride_token;
     float scale;
@@ -207,7 +207,9 @@ size_t nbx_paged_decode_workspace_bytes(int64_t rows, int32_t n_split, int32_t h
  *
  *   q            device, [batch, q_heads, q_rows, head_dim] contiguous, NBX_F32
  *                or NBX_BF16 (read exactly, never rounded).  Query row index
- *                row = (b * q_heads + h) * q_rows + r.
+ *                row = (b * q_heads + h) * q_rows + r.  At most 2^24 rows per
+ *                KV head ((q_heads / kv_heads) * q_rows), else
+ *                NBX_ERR_UNSUPPORTED.
  *   causal       0: every row of sequence b sees keys [0, seq_lens[b]).
  *                1: row r sees keys [0, seq_lens[b] - q_rows + r], i.e. the
  *                q_rows rows are the last q_rows positions of the sequence,

@@ -42,6 +42,9 @@ int check_pool(const nbx_kv_pool *p)
         return NBX_ERR_BAD_ALIGN;
     if (p->stride_token < p->head_dim || p->stride_head < 0 || p->stride_page < 0)
         return NBX_ERR_BAD_SHAPE;
+    // the kernels address the rows of a 16-row tile with 32-bit byte offsets
+    if (p->stride_token > ((int64_t)1 << 24))
+        return NBX_ERR_BAD_SHAPE;
     // 16-element strides and 16-byte base: every K/V row starts 16-byte aligned
     if (p->stride_token % 16 || p->stride_head % 16 || p->stride_page % 16 || !aligned16(p->data))
         return NBX_ERR_BAD_ALIGN;
@@ -291,6 +294,8 @@ static int validate_partial(const void *q, int32_t q_dtype, int32_t batch, int32
         return NBX_ERR_BAD_SHAPE;
     if (q_heads % k_pool->kv_heads)
         return NBX_ERR_BAD_SHAPE;
+    if ((int64_t)(q_heads / k_pool->kv_heads) * q_rows > ((int64_t)1 << 24))
+        return NBX_ERR_UNSUPPORTED;            // rows per KV head are counted in 32 bits
     if (scale != scale || scale == INFINITY || scale == -INFINITY)
         return NBX_ERR_BAD_SHAPE;
     if (split_size < 0 || split_size % 16)   // 0: derived on the device from seq_lens

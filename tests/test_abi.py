@@ -115,6 +115,8 @@ def partial_status(lib, k=None, v=None, q_dtype=1, batch=2, q_heads=4, q_rows=1,
     (dict(split=100), -4), (dict(split=-16), -4),
     (dict(n_split=0), -3),
     (dict(k=pool(stride_token=136)), -4),
+    (dict(k=pool(stride_token=(1 << 24) + 16)), -3),   # tiles use 32-bit byte offsets
+    (dict(q_rows=1 << 24), -6),                         # 2^25 rows per KV head
     (dict(k=pool(data=FAKE + 8)), -4),
     (dict(q=FAKE + 4), -4),
     (dict(k=pool(scale=0.0)), -3),
