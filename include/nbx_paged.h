@@ -241,7 +241,9 @@ size_t nbx_paged_decode_workspace_bytes(int64_t rows, int32_t n_split, int32_t h
  *                l = 0; its o is left unwritten (the merge never reads it).
  *
  * Supported: pool dtype NBX_F32 with any q dtype; NBX_BF16 or NBX_FP8_E4M3
- * pools with NBX_BF16 or NBX_F32 q.
+ * pools with NBX_BF16 or NBX_F32 q; n_split and batch * kv_heads each at
+ * most 65535 and batch * kv_heads * n_split below 2^31 (else
+ * NBX_ERR_BAD_SHAPE / NBX_ERR_UNSUPPORTED).
  */
 int nbx_paged_decode_partial(const void *q, int32_t q_dtype, int32_t batch, int32_t q_heads,
                              int32_t q_rows, int32_t causal, const nbx_kv_pool *k_pool,

@@ -304,6 +304,9 @@ static int validate_partial(const void *q, int32_t q_dtype, int32_t batch, int32
         return NBX_ERR_BAD_SHAPE;
     if ((int64_t)batch * k_pool->kv_heads > kMaxGridYZ)
         return NBX_ERR_UNSUPPORTED;
+    // (sequence, KV head, split) units are counted and enumerated in 32 bits
+    if ((int64_t)batch * k_pool->kv_heads * n_split > INT32_MAX)
+        return NBX_ERR_UNSUPPORTED;
     if ((int64_t)split_size * n_split > INT32_MAX || (int64_t)max_pages * k_pool->page_tokens > INT32_MAX)
         return NBX_ERR_BAD_SHAPE;
     if (!aligned16(q))

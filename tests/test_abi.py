@@ -117,6 +117,8 @@ def partial_status(lib, k=None, v=None, q_dtype=1, batch=2, q_heads=4, q_rows=1,
     (dict(k=pool(stride_token=136)), -4),
     (dict(k=pool(stride_token=(1 << 24) + 16)), -3),   # tiles use 32-bit byte offsets
     (dict(q_rows=1 << 24), -6),                         # 2^25 rows per KV head
+    (dict(batch=60000, n_split=40000, k=pool(kv_heads=1), v=pool(kv_heads=1),
+          q_heads=1), -6),                              # 2.4e9 (sequence, split) units
     (dict(k=pool(data=FAKE + 8)), -4),
     (dict(q=FAKE + 4), -4),
     (dict(k=pool(scale=0.0)), -3),
