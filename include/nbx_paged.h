@@ -66,7 +66,9 @@ typedef enum {
     NBX_ERR_BAD_ALIGN = -4,     /* page_tokens % 16, split_size % 16, split_size *
                                    n_split < the longest sequence, unit stride broken */
     NBX_ERR_WORKSPACE = -5,     /* workspace too small */
-    NBX_ERR_UNSUPPORTED = -6,   /* valid request this build does not implement */
+    NBX_ERR_UNSUPPORTED = -6,   /* valid request this build does not implement, or
+                                   whose grid exceeds the 2^32 work-items of one
+                                   dispatch */
     NBX_ERR_LAUNCH = -7         /* the HIP runtime refused a kernel launch */
 } nbx_status;
 
@@ -292,6 +294,8 @@ int nbx_paged_decode_partial_windows(const void *q, int32_t q_dtype, int32_t bat
  *                bf16 rounded to nearest even); head_dim is the partials'
  *                width Dv, 64, 128 or 256.
  *   n_split      at most 4096, else NBX_ERR_UNSUPPORTED.
+ *   rows         below 2^24 (one 256-thread workgroup per row), else
+ *                NBX_ERR_UNSUPPORTED.
  */
 int nbx_paged_decode_merge(const float *o_part, const float *m_part, const float *l_part,
                            int64_t rows, int32_t n_split, int32_t head_dim, void *out,

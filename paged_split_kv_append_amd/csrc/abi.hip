@@ -64,7 +64,14 @@ bool same_layout(const nbx_kv_pool *a, const nbx_kv_pool *b)
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-int to_status(hipError_t e) { return e == hipSuccess ? NBX_OK : NBX_ERR_LAUNCH; }
+// a grid beyond the dispatch limit (see grid_fits) is a request this build
+// does not serve; any other launch error is reported as such
+int to_status(hipError_t e)
+{
+    if (e == hipSuccess)
+        return NBX_OK;
+    return e == hipErrorInvalidConfiguration ? NBX_ERR_UNSUPPORTED : NBX_ERR_LAUNCH;
+}
 
 }  // namespace
 
@@ -445,8 +452,8 @@ int nbx_paged_decode_merge(const float *o_part, const float *m_part, const float
     if (!aligned16(o_part) || !aligned16(out) || ((uintptr_t)m_part & 3u) ||
         ((uintptr_t)l_part & 3u))
         return NBX_ERR_BAD_ALIGN;
-    if ((rows + 3) / 4 > INT32_MAX)
-        return NBX_ERR_BAD_SHAPE;
+    if (!nbx::grid_fits(rows, 256))              // one 256-thread workgroup per row
+        return NBX_ERR_UNSUPPORTED;
     nbx::MergeArgs a{o_part, m_part, l_part, rows, n_split, head_dim, out, out_dtype};
     return to_status(nbx::launch_merge(a, stream));
 }

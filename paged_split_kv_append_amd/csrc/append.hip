@@ -176,6 +176,8 @@ static hipError_t launch_append_t(const AppendArgs &a, hipStream_t stream)
 {
     const int32_t widest = a.new_v && a.v_head_dim > a.head_dim ? a.v_head_dim : a.head_dim;
     const int64_t total = a.n_tok * a.kv_heads * lanes_per_row(widest / 8);
+    if (!grid_fits((total + 255) / 256, 256))
+        return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)((total + 255) / 256), a.new_v ? 2 : 1);
     hipLaunchKernelGGL((paged_append_kernel<SRC, DST>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
@@ -262,6 +264,11 @@ kv_bounds_kernel(BoundsArgs a, int is_v)
 hipError_t launch_kv_bounds(const BoundsArgs &a, hipStream_t stream)
 {
     const int64_t n = (int64_t)a.num_pages * a.kv_heads;
+    for (int is_v = 0; is_v < 2; ++is_v) {
+        const int D = is_v ? a.v_head_dim : a.head_dim;
+        if (!grid_fits(((int64_t)a.kv_heads * a.page_tokens * lanes_per_row(D / 8) + 255) / 256, 256))
+            return hipErrorInvalidConfiguration;
+    }
     const unsigned zb = (unsigned)((n + 255) / 256 < 65535 ? (n + 255) / 256 : 65535);
     hipLaunchKernelGGL(fill_zero_kernel, dim3(zb), dim3(256), 0, stream, a.k_bounds, n);
     hipLaunchKernelGGL(fill_zero_kernel, dim3(zb), dim3(256), 0, stream, a.v_bounds, n);

@@ -135,6 +135,13 @@ struct BoundsArgs {
     int32_t max_pages, batch;
     int32_t *dev_err;
 };
+// A 1-D launch of `blocks` workgroups of `threads` fits the 32-bit work-item
+// count of a dispatch packet; launchers return hipErrorInvalidConfiguration
+// (NBX_ERR_UNSUPPORTED at the boundary) when it does not.
+inline bool grid_fits(int64_t blocks, int threads)
+{
+    return blocks >= 0 && blocks * threads <= (int64_t)0xFFFFFFFF;
+}
 hipError_t launch_kv_bounds(const BoundsArgs &a, hipStream_t stream);
 hipError_t launch_partial_valu(const PartialArgs &a, hipStream_t stream);
 // matrix-core partials (bf16 / fp8 pools, bf16 Q): more than 16 rows per KV

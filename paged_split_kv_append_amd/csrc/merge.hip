@@ -145,6 +145,8 @@ hipError_t launch_np(const MergeArgs &a, hipStream_t stream)
 {
     constexpr int LPS = D / 16, SPP = 64 / LPS;
     dim3 grid((unsigned)a.rows);
+    if (!grid_fits(a.rows, 256))
+        return hipErrorInvalidConfiguration;
     const int need = (a.n_split + SPP - 1) / SPP;
     if (need <= 1)
         hipLaunchKernelGGL((merge_kernel<D, OUT, 1>), grid, dim3(256), 0, stream, a);

@@ -819,7 +819,7 @@ hipError_t launch_kind(const PartialArgs &a, hipStream_t stream)
                                        : (a.max_pages * a.page_tokens + a.n_split - 1) / a.n_split;
     const int chunks = (split + kChunk - 1) / kChunk;
     const int64_t blocks = (int64_t)a.n_split * a.batch * a.kv_heads;
-    if (blocks > 0x7FFFFFFF)
+    if (!grid_fits(blocks, chunks >= 16 ? 256 : chunks >= 4 ? 128 : 64))
         return hipErrorInvalidConfiguration;
     dim3 grid((unsigned)blocks);
     if (chunks >= 16)

@@ -350,7 +350,7 @@ hipError_t launch_mr(const PartialArgs &a, hipStream_t stream)
     const int nt = multirow_tiles(M, D);
     const int row_blocks = multirow_row_blocks(M, D);
     const int64_t blocks = heads * row_blocks;
-    if (blocks > 0x7FFFFFFF)
+    if (!grid_fits(blocks, 512))
         return hipErrorInvalidConfiguration;
     if constexpr (D <= 128) {                 // two row tiles per wave only below D = 256
         if (nt == 2) {

@@ -137,6 +137,13 @@ def test_partial_validation(lib, kw, status):
     assert partial_status(lib, **kw) == status
 
 
+def test_oversized_grid_is_refused_before_any_launch(lib):
+    # 2^24 rows of one KV head in 65536 row blocks (256 rows each at D = 128)
+    # x 200 splits: 6.7e9 work-items of the multi-row kernel, beyond one dispatch
+    assert partial_status(lib, batch=1, q_heads=1, k=pool(kv_heads=1), v=pool(kv_heads=1),
+                          q_rows=1 << 24, n_split=200) == -6
+
+
 def test_append_validation(lib):
     k, v = pool(), pool()
     f = lambda nk=FAKE, nv=FAKE, dt=0, n=4, st=256, sh=128, kp=k, vp=v, sm=FAKE: \
@@ -177,6 +184,8 @@ def test_merge_validation(lib):
     assert m(ns=0) == -3
     assert m(ns=4097) == -6
     assert m(out=FAKE + 2) == -4
+    assert m(rows=-1) == -3
+    assert m(rows=1 << 24) == -6                 # 2^24 workgroups of 256 threads
 
 
 def test_one_call_workspace_checks(lib):
