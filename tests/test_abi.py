@@ -2,6 +2,7 @@
 symbol, its host-only functions agree with the oracle, and host validation
 refuses bad requests with the documented status before touching the device."""
 import ctypes
+import os
 
 import numpy as np
 import pytest
@@ -235,3 +236,20 @@ def test_windows_validation(lib):
     assert call(rows=None) == -1
     assert call(q_rows=0) == -3
     assert call(split=24) == -4
+
+
+def test_header_and_c_caller_compile_as_c():
+    """include/nbx_paged.h is a C header: the plain C caller compiles against it
+    with gcc in C11 with every warning an error."""
+    import importlib.util
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no gcc")
+    here = os.path.dirname(os.path.abspath(__file__))
+    spec = importlib.util.spec_from_file_location("build_check",
+                                                  os.path.join(here, "c", "build_check.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    r = subprocess.run(mod.flags(syntax_only=True), capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
