@@ -116,7 +116,24 @@ def _check(status: int, where: str):
 
 
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """Device pointer of a GPU tensor (every array argument of the C ABI is a
+    device pointer: a host tensor would hand a kernel a host address)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("every array argument must be a GPU tensor")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _int32_vector(t: torch.Tensor, n: int, name: str):
+    if t.dtype != torch.int32 or t.numel() != n or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 tensor of {n} elements")
+
+
+def _dev_err(t: Optional[torch.Tensor]):
+    if t is not None and (t.dtype != torch.int32 or t.numel() < 1):
+        raise ValueError("dev_err must be an int32 tensor of at least one element")
+    return _ptr(t)
 
 
 def _stream(stream) -> ctypes.c_void_p:
@@ -149,15 +166,16 @@ class KVPool:
 
     def desc(self) -> nbx_kv_pool:
         t = self.data
-        if t.dim() != 4 or t.stride(3) != 1:
-            raise ValueError("a pool is a [num_pages, kv_heads, page_tokens, head_dim] view "
+        if t.dim() != 4 or t.stride(3) != 1 or not t.is_cuda:
+            raise ValueError("a pool is a GPU [num_pages, kv_heads, page_tokens, head_dim] view "
                              "with a contiguous last dim")
         P, H, T, D = t.shape
         bp = None
         if self.bounds is not None:
             b = self.bounds
-            if b.dtype != torch.float32 or tuple(b.shape) != (P, H) or not b.is_contiguous():
-                raise ValueError("bounds must be a contiguous fp32 [num_pages, kv_heads] tensor")
+            if b.dtype != torch.float32 or tuple(b.shape) != (P, H) or not b.is_contiguous() \
+                    or not b.is_cuda:
+                raise ValueError("bounds must be a contiguous fp32 [num_pages, kv_heads] GPU tensor")
             bp = b.data_ptr()
         return nbx_kv_pool(t.data_ptr(), _dtype_code(t), P, H, T, D, t.stride(0), t.stride(1),
                            t.stride(2), float(self.scale), bp)
@@ -221,15 +239,27 @@ def nbx_paged_kv_append(new_k: torch.Tensor, new_v: Optional[torch.Tensor], k_po
         raise ValueError("new_v must match new_k in shape, strides and dtype")
     if new_k.shape[1] != k_pool.data.shape[1] or new_k.shape[2] != k_pool.data.shape[3]:
         raise ValueError("new positions do not fit the pool")
-    if slot_mapping.dtype != torch.int32 or slot_mapping.numel() != new_k.shape[0]:
-        raise ValueError("slot_mapping must be int32 [n_tok]")
+    _int32_vector(slot_mapping, new_k.shape[0], "slot_mapping")
     kd = k_pool.desc()
     vd = v_pool.desc() if v_pool is not None else None
     st = load_library().nbx_paged_kv_append(
         _ptr(new_k), _ptr(new_v), _dtype_code(new_k), new_k.shape[0], new_k.stride(0),
         new_k.stride(1), ctypes.byref(kd), ctypes.byref(vd) if vd is not None else None,
-        _ptr(slot_mapping), _ptr(dev_err), _stream(stream))
+        _ptr(slot_mapping), _dev_err(dev_err), _stream(stream))
     _check(st, "nbx_paged_kv_append")
+
+
+def _workspace_bytes(workspace) -> int:
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    return workspace.numel() * workspace.element_size()
+
+
+def _partials_shape(o_part, m_part, l_part, rows: int, n_split: int, dv: int):
+    for name, t, shape in (("o_part", o_part, (rows, n_split, dv)), ("m_part", m_part, (rows, n_split)),
+                           ("l_part", l_part, (rows, n_split))):
+        if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous fp32 {shape}")
 
 
 def _decode_common(q, k_pool, v_pool, block_table, seq_lens):
@@ -237,8 +267,7 @@ def _decode_common(q, k_pool, v_pool, block_table, seq_lens):
         raise ValueError("q is a contiguous [batch, q_heads, q_rows, head_dim] tensor")
     if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous():
         raise ValueError("block_table must be a contiguous int32 [batch, max_pages] tensor")
-    if seq_lens.dtype != torch.int32 or seq_lens.numel() != q.shape[0]:
-        raise ValueError("seq_lens must be int32 [batch]")
+    _int32_vector(seq_lens, q.shape[0], "seq_lens")
     if block_table.shape[0] != q.shape[0]:
         raise ValueError("block_table rows must equal the batch")
     return k_pool.desc(), v_pool.desc()
@@ -249,20 +278,19 @@ def nbx_paged_decode_partial(q, k_pool: KVPool, v_pool: KVPool, block_table, seq
                              causal: bool = False, dev_err=None, stream=None):
     kd, vd = _decode_common(q, k_pool, v_pool, block_table, seq_lens)
     B, Hq, W, _ = q.shape
-    rows, Dv = B * Hq * W, v_pool.data.shape[3]
-    for name, t, shape in (("o_part", o_part, (rows, n_split, Dv)), ("m_part", m_part, (rows, n_split)),
-                           ("l_part", l_part, (rows, n_split))):
-        if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous fp32 {shape}")
+    _partials_shape(o_part, m_part, l_part, B * Hq * W, n_split, v_pool.data.shape[3])
     st = load_library().nbx_paged_decode_partial(
         _ptr(q), _dtype_code(q), B, Hq, W, int(bool(causal)), ctypes.byref(kd), ctypes.byref(vd),
         _ptr(block_table), block_table.shape[1], _ptr(seq_lens), float(scale), int(split_size),
-        int(n_split), _ptr(o_part), _ptr(m_part), _ptr(l_part), _ptr(dev_err), _stream(stream))
+        int(n_split), _ptr(o_part), _ptr(m_part), _ptr(l_part), _dev_err(dev_err), _stream(stream))
     _check(st, "nbx_paged_decode_partial")
 
 
 def nbx_paged_decode_merge(o_part, m_part, l_part, out, stream=None):
+    if o_part.dim() != 3:
+        raise ValueError("o_part must be [rows, n_split, head_dim]")
     rows, n_split, D = o_part.shape
+    _partials_shape(o_part, m_part, l_part, rows, n_split, D)
     if out.shape[-1] != D or out.numel() != rows * D or not out.is_contiguous():
         raise ValueError("out must be contiguous with rows * head_dim elements")
     st = load_library().nbx_paged_decode_merge(_ptr(o_part), _ptr(m_part), _ptr(l_part), rows,
@@ -285,8 +313,8 @@ def nbx_paged_decode(q, k_pool: KVPool, v_pool: KVPool, block_table, seq_lens, s
     st = load_library().nbx_paged_decode(
         _ptr(q), _dtype_code(q), B, Hq, W, int(bool(causal)), ctypes.byref(kd), ctypes.byref(vd),
         _ptr(block_table), block_table.shape[1], _ptr(seq_lens), float(scale), int(split_size),
-        int(n_split), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
-        _dtype_code(out), _ptr(dev_err), _stream(stream))
+        int(n_split), _ptr(workspace), _workspace_bytes(workspace), _ptr(out),
+        _dtype_code(out), _dev_err(dev_err), _stream(stream))
     _check(st, "nbx_paged_decode")
 
 
@@ -317,8 +345,8 @@ def nbx_paged_decode_step(q, k_pool: KVPool, v_pool: KVPool, block_table, seq_le
         _ptr(q), _dtype_code(q), B, Hq, W, int(bool(causal)), _ptr(new_k), _ptr(new_v), new_dt,
         n_new, ctypes.byref(kd), ctypes.byref(vd), _ptr(block_table), block_table.shape[1],
         _ptr(seq_lens), float(scale), int(split_size), int(n_split), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _ptr(out),
-        _dtype_code(out) if out is not None else 0, _ptr(dev_err), _stream(stream))
+        _workspace_bytes(workspace), _ptr(out),
+        _dtype_code(out) if out is not None else 0, _dev_err(dev_err), _stream(stream))
     _check(st, "nbx_paged_decode_step")
 
 
@@ -345,12 +373,11 @@ def nbx_paged_kv_bounds(k_pool: KVPool, v_pool: KVPool, block_table, seq_lens, d
         raise ValueError("both pools need a bounds tensor")
     if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous():
         raise ValueError("block_table must be a contiguous int32 [batch, max_pages] tensor")
-    if seq_lens.dtype != torch.int32 or seq_lens.numel() != block_table.shape[0]:
-        raise ValueError("seq_lens must be int32 [batch]")
+    _int32_vector(seq_lens, block_table.shape[0], "seq_lens")
     kd, vd = k_pool.desc(), v_pool.desc()
     st = load_library().nbx_paged_kv_bounds(ctypes.byref(kd), ctypes.byref(vd), _ptr(block_table),
                                             block_table.shape[1], _ptr(seq_lens),
-                                            block_table.shape[0], _ptr(dev_err), _stream(stream))
+                                            block_table.shape[0], _dev_err(dev_err), _stream(stream))
     _check(st, "nbx_paged_kv_bounds")
 
 
@@ -370,12 +397,12 @@ def nbx_paged_decode_partial_windows(q, k_pool: KVPool, v_pool: KVPool, block_ta
     """Split partials with a window of rows_per_seq[b] rows for sequence b (q padded
     to [batch, q_heads, longest window, head_dim])."""
     kd, vd = _decode_common(q, k_pool, v_pool, block_table, seq_lens)
-    if rows_per_seq.dtype != torch.int32 or rows_per_seq.numel() != q.shape[0]:
-        raise ValueError("rows_per_seq must be int32 [batch]")
+    _int32_vector(rows_per_seq, q.shape[0], "rows_per_seq")
     B, Hq, W, D = q.shape
+    _partials_shape(o_part, m_part, l_part, B * Hq * W, n_split, v_pool.data.shape[3])
     st = load_library().nbx_paged_decode_partial_windows(
         _ptr(q), _dtype_code(q), B, Hq, W, _ptr(rows_per_seq), int(bool(causal)),
         ctypes.byref(kd), ctypes.byref(vd), _ptr(block_table), block_table.shape[1],
         _ptr(seq_lens), float(scale), int(split_size), int(n_split), _ptr(o_part), _ptr(m_part),
-        _ptr(l_part), _ptr(dev_err), _stream(stream))
+        _ptr(l_part), _dev_err(dev_err), _stream(stream))
     _check(st, "nbx_paged_decode_partial_windows")

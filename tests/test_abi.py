@@ -253,3 +253,25 @@ def test_header_and_c_caller_compile_as_c():
     spec.loader.exec_module(mod)
     r = subprocess.run(mod.flags(syntax_only=True), capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
+
+
+def test_binding_refuses_host_tensors_and_bad_vectors():
+    """The binding marshals device pointers only: a host tensor, a strided length
+    vector or undersized partials are refused before the library is called."""
+    import torch
+    q = torch.zeros(2, 4, 1, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        nb._ptr(q)
+    with pytest.raises(ValueError):
+        nb.KVPool(torch.zeros(8, 2, 16, 128, dtype=torch.bfloat16)).desc()
+    with pytest.raises(ValueError):
+        nb._int32_vector(torch.zeros(4, dtype=torch.int32)[::2], 2, "seq_lens")
+    with pytest.raises(ValueError):
+        nb._int32_vector(torch.zeros(2, dtype=torch.int64), 2, "seq_lens")
+    with pytest.raises(ValueError):
+        nb._dev_err(torch.zeros(0, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        nb._partials_shape(torch.zeros(8, 2, 128), torch.zeros(8, 1), torch.zeros(8, 2), 8, 2, 128)
+    with pytest.raises(ValueError):
+        nb._workspace_bytes(torch.zeros(64, dtype=torch.uint8)[::2])
+    assert nb._workspace_bytes(torch.zeros(16, dtype=torch.float32)) == 64
