@@ -56,11 +56,12 @@ __device__ __forceinline__ u32x4 vt_operand(const uint8_t *lane_base, int dt)
 
 // Online-softmax step for one lane's row over NK k-steps of 32 positions (two
 // 16-position tiles each): sc holds the scaled scores (log2 units, -inf where
-// masked).  Updates m, l, rescales o and returns the P operands of the k-steps
-// (hi and residual lo parts).
-template <int DT, bool PVS, int NK>
-__device__ __forceinline__ void softmax_step_n(float (&sc)[2 * NK][4], float &m_run, float &l_run,
-                                               f32x4 (&o)[DT], u32x4 (&ph)[NK], u32x4 (&pl)[NK])
+// masked).  Updates m and l, returns the P operands of the k-steps (hi and
+// residual lo parts) and the factor exp(m_old - m_new) by which the row's
+// accumulator must be scaled before this step's P V is added.
+template <bool PVS, int NK>
+__device__ __forceinline__ float softmax_corr_n(float (&sc)[2 * NK][4], float &m_run, float &l_run,
+                                                u32x4 (&ph)[NK], u32x4 (&pl)[NK])
 {
     float mx = sc[0][0];
 #pragma unroll
@@ -82,11 +83,6 @@ __device__ __forceinline__ void softmax_step_n(float (&sc)[2 * NK][4], float &m_
         }
     l_run = l_run * corr + psum;
     m_run = m_new;
-    if (__any(corr != 1.0f)) {             // a row's max moved: rescale (else o * 1 = o)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-            o[dt] *= corr;
-    }
 #pragma unroll
     for (int k = 0; k < NK; ++k)
 #pragma unroll
@@ -101,6 +97,21 @@ __device__ __forceinline__ void softmax_step_n(float (&sc)[2 * NK][4], float &m_
                     pack_bf16(p[t][2] - bf16_round(p[t][2]), p[t][3] - bf16_round(p[t][3]));
             }
         }
+    return corr;
+}
+
+// The same step with the row's accumulator o in this lane: it is rescaled when
+// some row's running max moved (else every factor is 1 and o * 1 = o).
+template <int DT, bool PVS, int NK>
+__device__ __forceinline__ void softmax_step_n(float (&sc)[2 * NK][4], float &m_run, float &l_run,
+                                               f32x4 (&o)[DT], u32x4 (&ph)[NK], u32x4 (&pl)[NK])
+{
+    const float corr = softmax_corr_n<PVS, NK>(sc, m_run, l_run, ph, pl);
+    if (__any(corr != 1.0f)) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+            o[dt] *= corr;
+    }
 }
 
 // ------------------------------------------------------------------ fixed shift

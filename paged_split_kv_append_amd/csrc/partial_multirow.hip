@@ -76,10 +76,12 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
 
     const int wb = seq_window(a, b, lead && s == 0 && rb == 0);
     int n_row[NT];
+    bool row_in[NT];                           // the lane's row of tile n is stored
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
         const int m = row_lo + (w * NT + n) * 16 + j;
-        n_row[n] = m < row_hi ? row_keys(a, L, wb, m % a.q_rows) : 0;
+        row_in[n] = m < row_hi;
+        n_row[n] = row_in[n] ? row_keys(a, L, wb, m % a.q_rows) : 0;
     }
     int n_max = 0;                             // the most keys a row of this block sees
     for (int m = row_lo; m < row_hi && m < row_lo + a.q_rows; ++m)
@@ -256,17 +258,37 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
                 for (int n = 0; n < NT; ++n)
                     acc[n][t] = mfma_bf16(ka, qb[n][kk], acc[n][t]);
             }
+        // Every position of the chunk visible to every stored row of the wave
+        // (all chunks of a split but its last ones and a causal window's
+        // edge): the scores need no mask.  Rows past the workgroup's last
+        // row are never stored and do not count.
+        bool lane_full = p0 + CH <= jend;
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+            lane_full = lane_full && (p0 + CH <= n_row[n] || !row_in[n]);
+#pragma unroll
+        for (int t = 0; t < TL; ++t)
+            lane_full = lane_full && ok[t];
+        const bool full = __all(lane_full);
         u32x4 ph[NT][NK], pl[NT][NK];
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
             const int e_n = min(jend, n_row[n]);
             float sc[TL][4];
+            if (full) {
 #pragma unroll
-            for (int t = 0; t < TL; ++t) {
+                for (int t = 0; t < TL; ++t)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int pos = p0 + 16 * t + 4 * g + i;
-                    sc[t][i] = (ok[t] && pos < e_n) ? acc[n][t][i] * scale2 : -INFINITY;
+                    for (int i = 0; i < 4; ++i)
+                        sc[t][i] = acc[n][t][i] * scale2;
+            } else {
+#pragma unroll
+                for (int t = 0; t < TL; ++t) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int pos = p0 + 16 * t + 4 * g + i;
+                        sc[t][i] = (ok[t] && pos < e_n) ? acc[n][t][i] * scale2 : -INFINITY;
+                    }
                 }
             }
             if (fixed[n])
