@@ -98,16 +98,21 @@ __device__ __forceinline__ u32x4 as_bf16x8(typename KvRaw<KVT>::type r)
         return widen8_e4m3(r);
 }
 
+// two floats rounded to bf16 (to nearest even), lo in the low half: one
+// v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
 {
-    const __bf16 a = (__bf16)lo, b = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
-__device__ __forceinline__ float bf16_round(float x)
+// {hi, lo} parts of a pair for the split P = hi + lo: lo holds the pair minus
+// its bf16 rounding (the rounded values are the bits of hi)
+__device__ __forceinline__ u32x2 pack_bf16_split(float x0, float x1)
 {
-    return (float)(__bf16)x;
+    const uint32_t hi = pack_bf16(x0, x1);
+    return u32x2{hi, pack_bf16(x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xFFFF0000u))};
 }
 
 __device__ __forceinline__ float fast_exp2(float x)

@@ -88,13 +88,16 @@ __device__ __forceinline__ float softmax_corr_n(float (&sc)[2 * NK][4], float &m
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int t = 2 * k + u;
-            ph[k][2 * u] = pack_bf16(p[t][0], p[t][1]);
-            ph[k][2 * u + 1] = pack_bf16(p[t][2], p[t][3]);
             if constexpr (PVS) {
-                pl[k][2 * u] =
-                    pack_bf16(p[t][0] - bf16_round(p[t][0]), p[t][1] - bf16_round(p[t][1]));
-                pl[k][2 * u + 1] =
-                    pack_bf16(p[t][2] - bf16_round(p[t][2]), p[t][3] - bf16_round(p[t][3]));
+                const u32x2 a = pack_bf16_split(p[t][0], p[t][1]);
+                const u32x2 c = pack_bf16_split(p[t][2], p[t][3]);
+                ph[k][2 * u] = a[0];
+                pl[k][2 * u] = a[1];
+                ph[k][2 * u + 1] = c[0];
+                pl[k][2 * u + 1] = c[1];
+            } else {
+                ph[k][2 * u] = pack_bf16(p[t][0], p[t][1]);
+                ph[k][2 * u + 1] = pack_bf16(p[t][2], p[t][3]);
             }
         }
     return corr;
@@ -198,13 +201,16 @@ __device__ __forceinline__ void softmax_fixed_n(float (&sc)[2 * NK][4], float m,
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int t = 2 * k + u;
-            ph[k][2 * u] = pack_bf16(p[t][0], p[t][1]);
-            ph[k][2 * u + 1] = pack_bf16(p[t][2], p[t][3]);
             if constexpr (PVS) {
-                pl[k][2 * u] =
-                    pack_bf16(p[t][0] - bf16_round(p[t][0]), p[t][1] - bf16_round(p[t][1]));
-                pl[k][2 * u + 1] =
-                    pack_bf16(p[t][2] - bf16_round(p[t][2]), p[t][3] - bf16_round(p[t][3]));
+                const u32x2 a = pack_bf16_split(p[t][0], p[t][1]);
+                const u32x2 c = pack_bf16_split(p[t][2], p[t][3]);
+                ph[k][2 * u] = a[0];
+                pl[k][2 * u] = a[1];
+                ph[k][2 * u + 1] = c[0];
+                pl[k][2 * u + 1] = c[1];
+            } else {
+                ph[k][2 * u] = pack_bf16(p[t][0], p[t][1]);
+                ph[k][2 * u + 1] = pack_bf16(p[t][2], p[t][3]);
             }
         }
 }
