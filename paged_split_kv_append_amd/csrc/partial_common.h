@@ -117,6 +117,76 @@ __device__ __forceinline__ void softmax_step_n(float (&sc)[2 * NK][4], float &m_
     }
 }
 
+// Lazy variant for the multi-row kernel: the row's shift m_run moves only when
+// the row's running maximum m_top has grown past it by more than kLazyShift
+// (log2 units), so p = 2^(s - m_run) stays below 2^kLazyShift and the
+// accumulator is rescaled on few chunks instead of on every chunk that raises
+// some row's maximum.  lazy_finish puts the partial in the exact-maximum form.
+constexpr float kLazyShift = 8.0f;
+
+template <bool PVS, int NK>
+__device__ __forceinline__ float softmax_lazy_n(float (&sc)[2 * NK][4], float &m_run, float &m_top,
+                                                float &l_run, u32x4 (&ph)[NK], u32x4 (&pl)[NK])
+{
+    float mx = sc[0][0];
+#pragma unroll
+    for (int t = 0; t < 2 * NK; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            mx = fmaxf(mx, sc[t][i]);
+    m_top = fmaxf(m_top, xor_max16_32(mx));
+    // m_run = -inf (no key yet): the difference is +inf and the shift moves;
+    // m_top = -inf too: NaN, and it stays
+    const float m_new = m_top - m_run > kLazyShift ? m_top : m_run;
+    const float m_safe = m_new == -INFINITY ? 0.0f : m_new;
+    const float corr = fast_exp2(m_run - m_safe);      // exactly 1 when the shift stays
+    float p[2 * NK][4], psum = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 2 * NK; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[t][i] = fast_exp2(sc[t][i] - m_safe);
+            psum += p[t][i];
+        }
+    l_run = l_run * corr + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int k = 0; k < NK; ++k)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int t = 2 * k + u;
+            if constexpr (PVS) {
+                const u32x2 a = pack_bf16_split(p[t][0], p[t][1]);
+                const u32x2 c = pack_bf16_split(p[t][2], p[t][3]);
+                ph[k][2 * u] = a[0];
+                pl[k][2 * u] = a[1];
+                ph[k][2 * u + 1] = c[0];
+                pl[k][2 * u + 1] = c[1];
+            } else {
+                ph[k][2 * u] = pack_bf16(p[t][0], p[t][1]);
+                ph[k][2 * u + 1] = pack_bf16(p[t][2], p[t][3]);
+            }
+        }
+    return corr;
+}
+
+// The lazy form's accumulator and sum rescaled from the shift m_run to the
+// row's maximum m_top (m_run <= m_top), so that the stored partial holds
+// m = the largest score, as the running-maximum form does.
+template <int DT>
+__device__ __forceinline__ void lazy_finish(float &m_run, float m_top, float &l_run,
+                                            f32x4 (&o)[DT])
+{
+    const float fin = m_top == -INFINITY ? 1.0f : fast_exp2(m_run - m_top);
+    l_run *= fin;
+    if (__any(fin != 1.0f)) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+            o[dt] *= fin;
+    }
+    m_run = m_top;
+}
+
 // ------------------------------------------------------------------ fixed shift
 //
 // The fixed-shift softmax of the maxdiffusion PR #477 page (fixed-m splash

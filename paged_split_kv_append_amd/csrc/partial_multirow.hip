@@ -101,11 +101,12 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
                                    : u32x4{0, 0, 0, 0};
     }
     const float scale2 = a.scale * a.k_scale * kLog2e;
-    float m_run[NT], l_run[NT];
+    float m_run[NT], m_top[NT], l_run[NT];     // shift (lazy), maximum, sum of each row
     f32x4 o[NT][DT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
         m_run[n] = -INFINITY;
+        m_top[n] = -INFINITY;
         l_run[n] = 0.0f;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
@@ -291,10 +292,17 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
                     }
                 }
             }
-            if (fixed[n])
+            if (fixed[n]) {
                 softmax_fixed_n<PVS, NK>(sc, m_fix[n], l_run[n], ph[n], pl[n]);
-            else
-                softmax_step_n<DT, PVS, NK>(sc, m_run[n], l_run[n], o[n], ph[n], pl[n]);
+            } else {
+                const float corr =
+                    softmax_lazy_n<PVS, NK>(sc, m_run[n], m_top[n], l_run[n], ph[n], pl[n]);
+                if (__any(corr != 1.0f)) {
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt)
+                        o[n][dt] *= corr;
+                }
+            }
         }
 #pragma unroll
         for (int kq = 0; kq < NK; ++kq)
@@ -345,6 +353,8 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
     const float vs = a.v_scale;
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
+        if (!fixed[n])
+            lazy_finish<DT>(m_run[n], m_top[n], l_run[n], o[n]);
         const float lt = xor_sum16_32(l_run[n]);
         const int m = row_lo + (w * NT + n) * 16 + j;
         if (m < row_hi) {
