@@ -11,7 +11,10 @@
 // Workgroups are ordered row block fastest and mapped so that the row blocks
 // of one split run on the same XCD and share its L2 (the rows-first order of
 // TensorFold PR #1219, made XCD-aware).  The fixed-shift softmax is taken
-// when both pools carry per-page bounds.
+// when both pools carry per-page bounds; otherwise the online softmax moves a
+// row's shift lazily (only when its maximum has grown by more than 2^8 in
+// log2 units) and puts the partial in the exact-maximum form before the
+// store.  Chunks that every stored row of a wave sees whole skip the mask.
 #include "partial_common.h"
 
 namespace nbx {
