@@ -459,3 +459,26 @@ def test_ragged_windows_full_size_sampled():
         r0, r1 = rows if rows else (0, g.shape[0])
         err = float(np.max(np.abs(g[r0:r1] - ref[r0:r1])))
         assert err <= TOL["bf16"], (b, err)
+
+
+DTYPE_MATRIX = [(kv, q, D, W) for kv in ("f32", "bf16", "fp8") for q in ("f32", "bf16")
+                for D in (64, 128) for W in (1, 5)]
+
+
+@pytest.mark.parametrize("kv,q,D,W", DTYPE_MATRIX,
+                         ids=[f"{kv}-q{q}-d{D}-w{W}" for kv, q, D, W in DTYPE_MATRIX])
+def test_dtype_matrix(kv, q, D, W):
+    """Every (pool dtype, Q dtype) pair the header supports, at two head dims, for
+    decode rows (W = 1: 4 rows per KV head) and a causal window (W = 5: 20 rows,
+    the multi-row kernel for 16/8-bit pools with bf16 Q; fp32 on either side
+    takes the vector-ALU kernel)."""
+    case = synth.make_case(2, batch=3, lens=("uniform", W, 400), kv_dtype=kv, q_dtype=q,
+                           head_dim=D, q_rows=W, causal=W > 1, append=False)
+    print(f"case kv={kv} q={q} D={D} W={W} lens={case.seq_lens.tolist()}", flush=True)
+    dc = DevCase(case)
+    out = dc.decode()
+    torch.cuda.synchronize()
+    ref, _, _ = _reference(case, dc)
+    assert dc.err_bits() == 0
+    err = max_abs(out, ref)
+    assert err <= TOL[kv], err
