@@ -52,6 +52,28 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c)
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Instruction order for a block of `reads` LDS operand reads feeding `reads /
+// per_read` groups of `mfma_per` products (group k using the reads k * per_read
+// .. k * per_read + per_read - 1): the first `ahead` groups' reads, then for
+// each further group one group of products and the next group's reads, then
+// the last products.  Each product then finds its operand read `ahead` groups
+// earlier, where the default schedule issued most reads just before their
+// product and waited on each.  Placed after the reads and products it orders,
+// in the same basic block; `id` keeps separate blocks apart.  (Masks of the
+// scheduling builtin: 0x100 LDS read, 0x008 MFMA.)
+template <int GROUPS, int PER_READ, int MFMA_PER, int AHEAD, int ID>
+__device__ __forceinline__ void schedule_reads_ahead()
+{
+    constexpr int A = AHEAD < GROUPS ? AHEAD : GROUPS;
+    __builtin_amdgcn_sched_group_barrier(0x100, A * PER_READ, ID);
+#pragma unroll
+    for (int i = 0; i < GROUPS - A; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, MFMA_PER, ID);
+        __builtin_amdgcn_sched_group_barrier(0x100, PER_READ, ID);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, A * MFMA_PER, ID);
+}
+
 // 8 E4M3FN codes (two dwords) widened to 8 bf16 (four dwords), exactly: every
 // E4M3FN value (subnormals included) is a bf16 value, so the hardware
 // conversion with scale 1 is exact; NaN codes give NaN.  Byte 2 k + h of a

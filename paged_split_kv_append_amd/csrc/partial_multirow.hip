@@ -262,6 +262,8 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
                 for (int n = 0; n < NT; ++n)
                     acc[n][t] = mfma_bf16(ka, qb[n][kk], acc[n][t]);
             }
+        // each K operand read one k-step (TL reads) ahead of its products
+        schedule_reads_ahead<KK * TL, 1, NT, TL, 0>();
         // Every position of the chunk visible to every stored row of the wave
         // (all chunks of a split but its last ones and a causal window's
         // edge): the scores need no mask.  Rows past the workgroup's last
@@ -319,6 +321,8 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
                         o[n][dt] = mfma_bf16(va, pl[n][kq], o[n][dt]);
                 }
             }
+        // each V operand (two transposing reads) four operands ahead of its products
+        schedule_reads_ahead<NK * DT, 2, NT * (PVS ? 2 : 1), 4, 1>();
     };
 
     // Iteration c: barrier (chunk c is in LDS buffer c & 1, every wave is done
