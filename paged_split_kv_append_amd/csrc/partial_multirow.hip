@@ -33,6 +33,8 @@ namespace {
 // of an operand read (8 rows, one piece each) then cover the 32 banks once.
 // (With (p + r / 4) & 3 two of those rows shared banks: the bank-conflict
 // counter read 28% of the LDS-active cycles, and the prompt chunk took 9% longer.)
+// Within each phase the LDS operand reads run ahead of the products that use
+// them (schedule_reads_ahead): K one k-step ahead, V four operands ahead.
 template <int D, int DV, int KVT, bool PVS, int NT, int NK, int NSET>
 __global__ void __launch_bounds__(512)
 multirow_mfma_kernel(PartialArgs a, int row_blocks)
