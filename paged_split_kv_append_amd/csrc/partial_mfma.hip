@@ -659,7 +659,7 @@ decode_persistent_kernel(PartialArgs a)
         const Item ci = cur;
         const int cc = c, cpg0 = pg0, cpg1 = pg1;
         land_v();                              // DS operations of the wave run in order
-        bool more = true, new_item = false;
+        bool more = true;
         if (c + 1 < cur.nchunk) {
             ++c;
             if ((c & 31) == 0)
@@ -669,7 +669,6 @@ decode_persistent_kernel(PartialArgs a)
             ++i_item;
             c = 0;
             pg_reg = pg_next;
-            new_item = true;
         } else {
             more = false;
         }
