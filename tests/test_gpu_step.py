@@ -83,6 +83,40 @@ def test_step_single_launch_matches_oracle(workload, seed):
                 case.slot_mapping)
 
 
+SWEEP = {
+    1: {},
+    2: REDUCED[2],
+    3: dict(batch=2, lens=("uniform", 300, 900)),
+    4: dict(lens=("fixed", 700)),
+    5: REDUCED[5],
+}
+
+
+@pytest.mark.parametrize("seed", range(102, 111))
+@pytest.mark.parametrize("workload", [1, 2, 3, 4, 5])
+def test_seed_sweep_step_matches_oracle(workload, seed):
+    """Seeds 102-110 of every shape (reduced in size, same structure: dtypes,
+    heads, page size, window rows, length distribution) through the step the
+    benchmark times: append and read where the shape appends, else partial and
+    merge; outputs against the oracle, pools bit for bit."""
+    case = synth.make_case(workload, seed=seed, **SWEEP[workload])
+    print(f"sweep workload={workload} seed={seed} lens={case.seq_lens.tolist()[:8]}", flush=True)
+    dc = DevCase(case)
+    out = dc.step()
+    torch.cuda.synchronize()
+    assert dc.err_bits() == 0
+    if case.new_k is not None:
+        _check_step(case, dc, out, case.new_k.unsqueeze(1), case.new_v.unsqueeze(1),
+                    case.slot_mapping)
+        return
+    ref = oracle.attention(case.q, case.q_dtype, case.k_pool, case.v_pool, case.kv_dtype,
+                           case.block_table, case.seq_lens, case.softmax_scale, case.causal,
+                           case.k_scale, case.v_scale)
+    assert torch.isfinite(out).all()
+    err = max_abs(out, ref)
+    assert err <= TOL[case.kv_dtype], f"max abs err {err}"
+
+
 @pytest.mark.parametrize("new_dtype", [torch.float32, torch.bfloat16])
 def test_step_bf16_new_tokens_and_fp8_pool(new_dtype):
     """bf16 new tokens (bit copy into a bf16 pool) and fp32/bf16 tokens into an fp8 pool."""
