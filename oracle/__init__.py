@@ -26,7 +26,7 @@ _lib = None
 
 MUTATIONS = {
     "none": 0, "drop_last_split": 1, "head_mod": 2, "causal_off_by_one": 3,
-    "swap_kv": 4, "shift_sign": 5, "page_offset": 6, "value_width": 7,
+    "swap_kv": 4, "shift_sign": 5, "page_offset": 6, "value_width": 7, "no_page_check": 8,
 }
 
 

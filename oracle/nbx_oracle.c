@@ -72,6 +72,7 @@ enum {
     ORC_MUT_NO_MAX_SHIFT_SIGN = 5, /* exp(m - s) instead of exp(s - m) */
     ORC_MUT_PAGE_OFFSET = 6,       /* position in page taken as j mod T + 1 (wraps) */
     ORC_MUT_V_WIDTH = 7,           /* V rows addressed with the q/k head dim D, not Dv */
+    ORC_MUT_NO_PAGE_CHECK = 8,     /* an unmapped (-1) page read as a page of the pool */
 };
 static int g_mutation = ORC_MUT_NONE;
 
@@ -290,6 +291,8 @@ static int64_t gather_offset(const orc_problem *pr, int b, int g, int64_t j, int
     int64_t pos = j % pr->T;
     if (g_mutation == ORC_MUT_PAGE_OFFSET)
         pos = (pos + 1) % pr->T;
+    if (g_mutation == ORC_MUT_NO_PAGE_CHECK)   /* wraps like a negative array index */
+        page = ((page % pr->P) + pr->P) % pr->P;
     if (page < 0 || page >= pr->P)
         return -1;
     return ((page * pr->Hkv + g) * pr->T + pos) * width + e;

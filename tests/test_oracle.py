@@ -514,6 +514,15 @@ def _pins_pass():
         ok.append(np.allclose(oracle_on(p, 0.25), sdpa_reference(p, 0.25), atol=1e-10))
     except ValueError:                    # a planted mistake the oracle refuses to run
         ok.append(False)
+    # a -1 entry inside a sequence's range maps no page: the oracle must refuse it
+    p = contiguous_problem(44, B=2, Hq=2, Hkv=1, W=1, D=16, lens=(35, 50))
+    p["bt"] = p["bt"].copy()
+    p["bt"][1, 1] = -1
+    try:
+        oracle_on(p, 0.25)
+        ok.append(False)
+    except ValueError:
+        ok.append(True)
     return all(ok), ok
 
 
@@ -522,7 +531,8 @@ def test_pins_pass_without_mutation():
 
 
 @pytest.mark.parametrize("name", ["drop_last_split", "head_mod", "causal_off_by_one",
-                                  "swap_kv", "shift_sign", "page_offset", "value_width"])
+                                  "swap_kv", "shift_sign", "page_offset", "value_width",
+                                  "no_page_check"])
 def test_planted_mistake_goes_red(name):
     with oracle.mutation(name):
         passed, detail = _pins_pass()
