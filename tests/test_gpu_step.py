@@ -83,6 +83,34 @@ def test_step_single_launch_matches_oracle(workload, seed):
                 case.slot_mapping)
 
 
+@pytest.mark.parametrize("batch,kv_dtype", [(65, "bf16"), (200, "fp8"), (256, "bf16")])
+def test_step_batches_past_one_lane_block(batch, kv_dtype):
+    """65 to 256 sequences: the single-launch step's sequence table (one lane
+    per sequence) spans several 64-lane blocks; batch 256 is the largest it
+    takes.  Appended rows bit for bit, outputs against the oracle."""
+    case = synth.make_case(2, seed=90 + batch, kv_dtype=kv_dtype, batch=batch,
+                           lens=("uniform", 1, 300))
+    print(f"step batch={batch} {kv_dtype}", flush=True)
+    dc = DevCase(case)
+    out = dc.step()
+    torch.cuda.synchronize()
+    assert dc.err_bits() == 0
+    _check_step(case, dc, out, case.new_k.unsqueeze(1), case.new_v.unsqueeze(1),
+                case.slot_mapping)
+
+
+def test_step_value_head_dim_batch_past_one_lane_block():
+    """The 192 / 128 K / V pair with 129 sequences through the single-launch step."""
+    case = synth.make_case(7, seed=97, batch=129, lens=("uniform", 1, 200))
+    print(f"step 192/128 batch={case.batch}", flush=True)
+    dc = DevCase(case)
+    out = dc.step()
+    torch.cuda.synchronize()
+    assert dc.err_bits() == 0
+    _check_step(case, dc, out, case.new_k.unsqueeze(1), case.new_v.unsqueeze(1),
+                case.slot_mapping)
+
+
 SWEEP = {
     1: {},
     2: REDUCED[2],
