@@ -111,6 +111,25 @@ def test_step_value_head_dim_batch_past_one_lane_block():
                 case.slot_mapping)
 
 
+@pytest.mark.parametrize("workload,over", [
+    (3, dict(q_rows=1, causal=False, batch=5, lens=("uniform", 1, 900))),
+    (4, dict(q_rows=2, causal=True, batch=3, lens=("uniform", 2, 900))),
+], ids=["d256_bf16_decode", "d256_fp8_window2"])
+def test_step_head_dim_256_single_launch(workload, over):
+    """D = 256 with at most 16 rows per KV head (6 GQA heads x 1 or 2 window
+    rows) takes the single-launch step with the fused append: bf16 and fp8
+    pools, appended rows bit for bit, outputs against the oracle."""
+    case = synth.make_case(workload, seed=98 + workload, append=True, **over)
+    print(f"step d256 workload={workload} rows/kv={case.q_heads // case.kv_heads * case.q_rows}",
+          flush=True)
+    dc = DevCase(case)
+    out = dc.step()
+    torch.cuda.synchronize()
+    assert dc.err_bits() == 0
+    _check_step(case, dc, out, case.new_k.unsqueeze(1), case.new_v.unsqueeze(1),
+                case.slot_mapping)
+
+
 SWEEP = {
     1: {},
     2: REDUCED[2],
