@@ -130,6 +130,20 @@ def test_step_head_dim_256_single_launch(workload, over):
                 case.slot_mapping)
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_step_head_dim_64_single_launch(kv_dtype):
+    """D = 64 through the single-launch step with the fused append."""
+    case = synth.make_case(2, seed=96, kv_dtype=kv_dtype, head_dim=64, batch=7,
+                           lens=("uniform", 1, 600))
+    print(f"step d64 {kv_dtype}", flush=True)
+    dc = DevCase(case)
+    out = dc.step()
+    torch.cuda.synchronize()
+    assert dc.err_bits() == 0
+    _check_step(case, dc, out, case.new_k.unsqueeze(1), case.new_v.unsqueeze(1),
+                case.slot_mapping)
+
+
 SWEEP = {
     1: {},
     2: REDUCED[2],
