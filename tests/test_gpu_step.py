@@ -99,10 +99,12 @@ def test_step_batches_past_one_lane_block(batch, kv_dtype):
                 case.slot_mapping)
 
 
-def test_step_value_head_dim_batch_past_one_lane_block():
-    """The 192 / 128 K / V pair with 129 sequences through the single-launch step."""
-    case = synth.make_case(7, seed=97, batch=129, lens=("uniform", 1, 200))
-    print(f"step 192/128 batch={case.batch}", flush=True)
+@pytest.mark.parametrize("batch,kv_dtype", [(129, "bf16"), (9, "fp8")])
+def test_step_value_head_dim_single_launch(batch, kv_dtype):
+    """The 192 / 128 K / V pair through the single-launch step: 129 sequences
+    (past one 64-lane block of the sequence table) and an fp8 pool."""
+    case = synth.make_case(7, seed=97, kv_dtype=kv_dtype, batch=batch, lens=("uniform", 1, 200))
+    print(f"step 192/128 batch={case.batch} {kv_dtype}", flush=True)
     dc = DevCase(case)
     out = dc.step()
     torch.cuda.synchronize()
