@@ -319,6 +319,12 @@ MULTIROW = [
                             lens=("uniform", 6, 800), append=False)),
     ("d128_fp8_noncausal_80rows", dict(batch=2, kv_dtype="fp8", q_rows=20, causal=False,
                                        lens=("uniform", 1, 600), append=False)),
+    # two row tiles per wave (more than 128 rows, D <= 128): fp8, and a second
+    # 256-row block holding 32 rows, so that most of its waves have none
+    ("d128_fp8_160rows", dict(batch=2, kv_dtype="fp8", q_rows=40, causal=True,
+                              lens=("uniform", 40, 700), append=False)),
+    ("d64_bf16_288rows", dict(batch=2, head_dim=64, q_rows=72, causal=True,
+                              lens=("uniform", 72, 600), append=False)),
 ]
 
 
