@@ -11,7 +11,7 @@
 namespace {
 
 constexpr int kMaxGridYZ = 65535;
-constexpr int kMaxMergeSplits = 4096;   // the merge keeps one weight per split in LDS
+constexpr int kMaxMergeSplits = 4096;   // the most splits the merge takes (past 64 it loops)
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -591,7 +591,7 @@ int nbx_paged_decode_step(const void *q, int32_t q_dtype, int32_t batch, int32_t
             e = launch_partial(a, stream);
     }
     if (e != hipSuccess)
-        return NBX_ERR_LAUNCH;
+        return to_status(e);
     if (!out)
         return NBX_OK;                         // partials only, left in the workspace
     nbx::MergeArgs m{o_part, m_part, l_part, rows, n_split, Dv, out, out_dtype};

@@ -34,6 +34,12 @@ __device__ u32x4 nbx_buffer_load_b128(i32x4 rsrc, int voffset, int soffset, int 
 __device__ u32x2 nbx_buffer_load_b64(i32x4 rsrc, int voffset, int soffset, int aux)
     __asm("llvm.amdgcn.raw.buffer.load.v2i32");
 
+// Cache policy of the K/V tile loads (the aux operand of the buffer loads;
+// bit 1 is gfx950's nt): each K/V byte is read once per launch, so the loads
+// are marked non-temporal and the lines are not kept in the L2 or the
+// last-level cache for reuse.
+constexpr int kStreamAux = 2;
+
 // Descriptor for `bytes` bytes from `base` (uniform values; forced to SGPRs).
 __device__ __forceinline__ i32x4 make_buffer_rsrc(const void *base, uint32_t bytes)
 {
@@ -106,9 +112,9 @@ template <int KVT>
 __device__ __forceinline__ typename KvRaw<KVT>::type buffer_load8_raw(i32x4 rsrc, int voff)
 {
     if constexpr (KVT == NBX_BF16)
-        return nbx_buffer_load_b128(rsrc, voff, 0, 0);
+        return nbx_buffer_load_b128(rsrc, voff, 0, kStreamAux);
     else
-        return nbx_buffer_load_b64(rsrc, voff, 0, 0);
+        return nbx_buffer_load_b64(rsrc, voff, 0, kStreamAux);
 }
 
 template <int KVT>

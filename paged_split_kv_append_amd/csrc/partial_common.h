@@ -38,6 +38,105 @@ __device__ __forceinline__ int tile_page(const PartialArgs &a, int b, int ts, in
     return page;
 }
 
+// Buffer descriptor of tile rows [0, rows) starting at position ts in `page`
+// (rows <= 0 or an unmapped page gives an empty range).
+template <int ESZ>
+__device__ __forceinline__ i32x4 tile_rsrc(const void *data, int64_t stride_page,
+                                           int64_t head_off, int64_t stride_token, int page_tokens,
+                                           int page, int ts, int rows)
+{
+    const int pg = page >= 0 ? page : 0;
+    const int64_t off = (int64_t)(ts % page_tokens);
+    const uint8_t *base =
+        (const uint8_t *)data + ((int64_t)pg * stride_page + head_off + off * stride_token) * ESZ;
+    const uint32_t bytes = page >= 0 && rows > 0 ? (uint32_t)(rows * stride_token * ESZ) : 0u;
+    return make_buffer_rsrc(base, bytes);
+}
+
+// One new K or V row (D elements at src of a [.., D] array of src_dtype)
+// stored at element offset dst of a bf16 or fp8 pool, with the append's
+// conversions: bf16 -> bf16 bit copy, fp32 -> bf16 round to nearest even, to
+// fp8 the correctly rounded quotient value / scale, rounded to nearest even
+// and saturated.  Lane l stores elements l * D/64 .. (l + 1) * D/64 - 1.
+// Returns the lane's share of the stored row's bound statistic (stored
+// units): the sum of squares (K) or the largest magnitude (V).
+template <int D, int KVT, bool V>
+__device__ __forceinline__ float store_new_row(const void *src_base, int src_dtype, int64_t src,
+                                               void *pool, int64_t dst, float scale, int lane)
+{
+    constexpr int E = D / 64;
+    float stat = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int64_t i = lane * E + e;
+        float stored;
+        if constexpr (KVT == NBX_BF16) {
+            const uint16_t bits = src_dtype == NBX_BF16
+                                      ? ((const uint16_t *)src_base)[src + i]
+                                      : f32_to_bf16_bits(((const float *)src_base)[src + i]);
+            ((uint16_t *)pool)[dst + i] = bits;
+            stored = bf16_bits_to_f32(bits);
+        } else {
+            const float x = src_dtype == NBX_BF16
+                                ? bf16_bits_to_f32(((const uint16_t *)src_base)[src + i])
+                                : ((const float *)src_base)[src + i];
+            const uint8_t code = f32_to_e4m3(__fdiv_rn(x, scale));
+            ((uint8_t *)pool)[dst + i] = code;
+            stored = e4m3_to_f32(code);
+        }
+        stat = V ? bound_max(stat, fabsf(stored)) : fmaf(stored, stored, stat);
+    }
+    return stat;
+}
+
+// Whole-row loads of a 16-row bf16 tile of DW columns: load i of a wave
+// (64 lanes x 16 bytes) takes the 16-byte units 64 i .. 64 i + 63 of the tile
+// in row-major order, i.e. whole rows (4 of 256 bytes at DW = 128), so every
+// load fetches complete 128-byte lines.  In LDS the tile is row-major with
+// unit u of row r stored at unit (u + rot r) mod U of that row (U units per
+// row, rot = 2 for U >= 16, else 1): the 16 lanes landing one row write 16
+// different units, the 8 lanes of a K operand read (8 rows, one unit each)
+// fall on different banks, and so do the 4-row pieces of a transposed V read.
+template <int DW>
+struct RowTile {
+    static constexpr int U = DW / 8;           // 16-byte units per row
+    static constexpr int ROT = U >= 16 ? 2 : 1;
+    static constexpr int ROWB = DW * 2;        // bytes per row in LDS
+    int lane, stride_b;                        // row stride of the pool in bytes
+    __device__ RowTile(int lane_, int stride_b_) : lane(lane_), stride_b(stride_b_) {}
+    // LDS offset of unit u of row r
+    __device__ static int at(int r, int u) { return r * ROWB + ((u + ROT * r) % U) * 16; }
+    // byte offset in the pool of this lane's piece of load i
+    __device__ int global(int i) const
+    {
+        const int x = 64 * i + lane;
+        return (x / U) * stride_b + (x % U) * 16;
+    }
+    // LDS offset of the same piece
+    __device__ int lds(int i) const
+    {
+        const int x = 64 * i + lane;
+        return at(x / U, x % U);
+    }
+    // A operand of S^T = K Q^T (lane 16 g + j: row j, unit u = 4 kk + g)
+    __device__ int operand(int r, int u) const { return at(r, u); }
+    // A operand of O^T += V^T P^T for 16-column slice dt from the two tiles
+    // of a chunk (the second `half` bytes after the first): lane 16 g + j
+    // reads row 4 g + j / 4, columns 16 dt + 4 (j % 4) .. + 3 of each, and the
+    // transposing read hands it column 16 dt + j of rows 4 g .. 4 g + 3
+    __device__ u32x4 transposed(const uint8_t *tile, int half, int g, int j, int dt) const
+    {
+        const uint8_t *p0 = tile + at(4 * g + (j >> 2), 2 * dt + ((j & 3) >> 1)) + (j & 1) * 8;
+        const uint8_t *p1 = p0 + half;
+        const bf16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4 *)(__attribute__((address_space(3))) uint8_t *)p0);
+        const bf16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_bf16x4 *)(__attribute__((address_space(3))) uint8_t *)p1);
+        const u32x2 ux = __builtin_bit_cast(u32x2, x), uy = __builtin_bit_cast(u32x2, y);
+        return u32x4{ux[0], ux[1], uy[0], uy[1]};
+    }
+};
+
 // A operand of the P V product for 16-column slice dt from a column-blocked
 // chunk tile (tile 0 blocks, then tile 1 blocks); `lane_base` is the lane's
 // fixed address: block 0 of tile 0 + (4 g + j/4) * 32 + (j % 4) * 8.

@@ -70,21 +70,6 @@ __device__ __forceinline__ int chunk_pages(const PartialArgs &a, int b, int j0, 
     return cq < nchunk ? tile_page(a, b, ts, jend, flag_it) : -1;
 }
 
-// Buffer descriptor of tile rows [0, rows) starting at position ts in `page`
-// (rows <= 0 or an unmapped page gives an empty range).
-template <int ESZ>
-__device__ __forceinline__ i32x4 tile_rsrc(const void *data, int64_t stride_page,
-                                           int64_t head_off, int64_t stride_token, int page_tokens,
-                                           int page, int ts, int rows)
-{
-    const int pg = page >= 0 ? page : 0;
-    const int64_t off = (int64_t)(ts % page_tokens);
-    const uint8_t *base =
-        (const uint8_t *)data + ((int64_t)pg * stride_page + head_off + off * stride_token) * ESZ;
-    const uint32_t bytes = page >= 0 && rows > 0 ? (uint32_t)(rows * stride_token * ESZ) : 0u;
-    return make_buffer_rsrc(base, bytes);
-}
-
 // Online-softmax step for one lane's row over the 32 positions of a chunk
 // (softmax_step_n with one k-step): returns the P operand (hi and residual lo).
 template <int DT, bool PVS>
@@ -188,9 +173,9 @@ decode_mfma_kernel(PartialArgs a)
             for (int k = 0; k < DT / 2; ++k) {
                 const int i = t * (DT / 2) + k;
                 if constexpr (BF)
-                    vr[i] = nbx_buffer_load_b128(rv, v_lane + k * 64, 0, 0);
+                    vr[i] = nbx_buffer_load_b128(rv, v_lane + k * 64, 0, kStreamAux);
                 else
-                    vraw[i] = nbx_buffer_load_b64(rv, v_lane + k * 32, 0, 0);
+                    vraw[i] = nbx_buffer_load_b64(rv, v_lane + k * 32, 0, kStreamAux);
             }
         }
     };
@@ -324,42 +309,6 @@ decode_mfma_kernel(PartialArgs a)
 
 // ------------------------------------------------------------------ persistent decode
 
-// One new K or V row (D elements at src of a [.., D] array of src_dtype)
-// stored at element offset dst of a bf16 or fp8 pool, with the append's
-// conversions: bf16 -> bf16 bit copy, fp32 -> bf16 round to nearest even, to
-// fp8 the correctly rounded quotient value / scale, rounded to nearest even
-// and saturated.  Lane l stores elements l * D/64 .. (l + 1) * D/64 - 1.
-// Returns the lane's share of the stored row's bound statistic (stored
-// units): the sum of squares (K) or the largest magnitude (V).
-template <int D, int KVT, bool V>
-__device__ __forceinline__ float store_new_row(const void *src_base, int src_dtype, int64_t src,
-                                               void *pool, int64_t dst, float scale, int lane)
-{
-    constexpr int E = D / 64;
-    float stat = 0.0f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int64_t i = lane * E + e;
-        float stored;
-        if constexpr (KVT == NBX_BF16) {
-            const uint16_t bits = src_dtype == NBX_BF16
-                                      ? ((const uint16_t *)src_base)[src + i]
-                                      : f32_to_bf16_bits(((const float *)src_base)[src + i]);
-            ((uint16_t *)pool)[dst + i] = bits;
-            stored = bf16_bits_to_f32(bits);
-        } else {
-            const float x = src_dtype == NBX_BF16
-                                ? bf16_bits_to_f32(((const uint16_t *)src_base)[src + i])
-                                : ((const float *)src_base)[src + i];
-            const uint8_t code = f32_to_e4m3(__fdiv_rn(x, scale));
-            ((uint8_t *)pool)[dst + i] = code;
-            stored = e4m3_to_f32(code);
-        }
-        stat = V ? bound_max(stat, fabsf(stored)) : fmaf(stored, stored, stat);
-    }
-    return stat;
-}
-
 constexpr int kPersistMaxBatch = 256;      // sequences covered by the lane-register item table
 
 // One wave per work item = (sequence b, split s, KV head g) with keys in the
@@ -378,14 +327,20 @@ constexpr int kPersistMaxBatch = 256;      // sequences covered by the lane-regi
 // registers without spilling; left to itself the compiler takes one more
 // AGPR block and halves the resident waves).
 template <int D, int DV, int KVT, bool PVS, int NB, bool FA, bool BND>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu((BND && D == 128) ? 2 : 1)))
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(((BND || KVT == NBX_BF16) && D == 128) ? 2 : 1)))
 decode_persistent_kernel(PartialArgs a)
 {
     constexpr int KK = D / 32, DT = DV / 16;
     constexpr bool BF = KVT == NBX_BF16;
     constexpr int ESZ = BF ? 2 : 1;
     constexpr int VBYTES = kChunk * 2 * DV;
+    // bf16 pools: K and V tiles are loaded as whole rows (rows_k / rows_v
+    // below) and K is read back from LDS; fp8 pools load each operand's
+    // 16 x 64-byte piece straight into registers
+    constexpr bool RM = BF;
+    constexpr int KBYTES = RM ? kChunk * 2 * D : 16;
     __shared__ __attribute__((aligned(16))) uint8_t tile[VBYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t ktile[KBYTES];
 
     const int lane = threadIdx.x;
     const int g = lane >> 4, j = lane & 15;
@@ -571,11 +526,14 @@ decode_persistent_kernel(PartialArgs a)
     const int k_lane = j * kst_b + g * 8 * ESZ;                        // + kk * 32 * ESZ
     const int v_lane = ((lane & 31) >> 1) * vst_b + ((lane >> 5) * 16 + (lane & 1) * 8) * ESZ;
     const uint8_t *vt_lane = tile + (4 * g + (j >> 2)) * 32 + (j & 3) * 8;
+    const RowTile<D> rows_k(lane, kst_b);
+    const RowTile<DV> rows_v(lane, vst_b);
     const float scale2 = a.scale * a.k_scale * kLog2e;
     const float vs = a.v_scale;
 
     typename KvRaw<KVT>::type kr[2][KK];       // K as loaded; widened at its use
     u32x4 qb[KK];
+    u32x4 qn[RM ? KK : 1];                     // bf16: the next chunk's Q, loaded with its K
     u32x4 vr[BF ? DT : 1];
     u32x2 vraw[BF ? 1 : DT];
     auto issue_v = [&](const Item &it, int c, int pg0, int pg1) {
@@ -589,17 +547,23 @@ decode_persistent_kernel(PartialArgs a)
 #pragma unroll
             for (int k = 0; k < DT / 2; ++k) {
                 const int i = t * (DT / 2) + k;
-                if constexpr (BF)
-                    vr[i] = nbx_buffer_load_b128(rv, v_lane + k * 64, 0, 0);
+                if constexpr (RM)
+                    vr[i] = nbx_buffer_load_b128(rv, rows_v.global(k), 0, kStreamAux);
+                else if constexpr (BF)
+                    vr[i] = nbx_buffer_load_b128(rv, v_lane + k * 64, 0, kStreamAux);
                 else
-                    vraw[i] = nbx_buffer_load_b64(rv, v_lane + k * 32, 0, 0);
+                    vraw[i] = nbx_buffer_load_b64(rv, v_lane + k * 32, 0, kStreamAux);
             }
         }
     };
     // K rows of the chunk and, with them, the item's Q rows (a few KB that stay
-    // in L2): one register set each, refilled right after the scores are formed
+    // in L2): one register set each; for fp8 refilled right after the scores
+    // are formed, for bf16 (K landed in LDS) with the V rows
     auto issue_k = [&](const Item &it, int c, int pg0, int pg1) {
-        load_q(it, qb);
+        if constexpr (!RM)
+            load_q(it, qb);
+        else if (c == 0)                       // a new item: its Q, taken up at its first chunk
+            load_q(it, qn);
         const int p0 = it.j0 + c * kChunk;
         const int64_t k_head = (int64_t)it.gk * a.k_stride_head;
 #pragma unroll
@@ -607,21 +571,53 @@ decode_persistent_kernel(PartialArgs a)
             const i32x4 rk = tile_rsrc<ESZ>(a.k_data, a.k_stride_page, k_head, a.k_stride_token,
                                             a.page_tokens, t ? pg1 : pg0, p0 + 16 * t, 16);
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk)
-                kr[t][kk] = buffer_load8_raw<KVT>(rk, k_lane + kk * 32 * ESZ);
+            for (int kk = 0; kk < KK; ++kk) {
+                if constexpr (RM)
+                    kr[t][kk] = nbx_buffer_load_b128(rk, rows_k.global(kk), 0, kStreamAux);
+                else
+                    kr[t][kk] = buffer_load8_raw<KVT>(rk, k_lane + kk * 32 * ESZ);
+            }
         }
     };
     auto land_v = [&]() {
 #pragma unroll
         for (int i = 0; i < DT; ++i) {
             const int t = i / (DT / 2), k = i % (DT / 2);
-            u32x4 v;
-            if constexpr (BF)
-                v = vr[i];
-            else
-                v = widen8_e4m3(vraw[i]);
-            *(u32x4 *)(tile + t * DT * 512 + k * 1024 + lane * 16) = v;
+            if constexpr (RM) {
+                *(u32x4 *)(tile + t * (VBYTES / 2) + rows_v.lds(k)) = vr[i];
+            } else {
+                u32x4 v;
+                if constexpr (BF)
+                    v = vr[i];
+                else
+                    v = widen8_e4m3(vraw[i]);
+                *(u32x4 *)(tile + t * DT * 512 + k * 1024 + lane * 16) = v;
+            }
         }
+    };
+    auto land_k = [&]() {
+        if constexpr (RM) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk)
+                    *(u32x4 *)(ktile + t * (KBYTES / 2) + rows_k.lds(kk)) = kr[t][kk];
+        }
+    };
+    // A operand of S^T = K Q^T for k-step kk of tile t: lane (g, j) takes
+    // row j, columns 32 kk + 8 g .. + 7 (from LDS for bf16)
+    auto k_operand = [&](int t, int kk) {
+        if constexpr (RM)
+            return *(const u32x4 *)(ktile + t * (KBYTES / 2) + rows_k.operand(j, 4 * kk + g));
+        else
+            return as_bf16x8<KVT>(kr[t][kk]);
+    };
+    // A operand of O^T += V^T P^T for 16-column slice dt (both tiles)
+    auto v_operand = [&](int dt) {
+        if constexpr (RM)
+            return rows_v.transposed(tile, VBYTES / 2, g, j, dt);
+        else
+            return vt_operand<DT>(vt_lane, dt);
     };
 
     float m_run = -INFINITY, l_run = 0.0f;
@@ -659,6 +655,14 @@ decode_persistent_kernel(PartialArgs a)
         const Item ci = cur;
         const int cc = c, cpg0 = pg0, cpg1 = pg1;
         land_v();                              // DS operations of the wave run in order
+        land_k();
+        if constexpr (RM) {
+            if (cc == 0) {                     // the item's Q (loaded before its K)
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk)
+                    qb[kk] = qn[kk];
+            }
+        }
         bool more = true;
         if (c + 1 < cur.nchunk) {
             ++c;
@@ -676,6 +680,11 @@ decode_persistent_kernel(PartialArgs a)
             pg0 = __builtin_amdgcn_readlane(pg_reg, 2 * (c & 31));
             pg1 = __builtin_amdgcn_readlane(pg_reg, 2 * (c & 31) + 1);
             issue_v(cur, c, pg0, pg1);
+            if constexpr (RM) {               // K(c) is in LDS: its registers are free
+                issue_k(cur, c, pg0, pg1);
+                if (c == cur.nchunk - 1)
+                    prepare_next();
+            }
         }
         const int p0 = ci.j0 + cc * kChunk;
         float sc[2][4];
@@ -684,7 +693,7 @@ decode_persistent_kernel(PartialArgs a)
             f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk)
-                acc = mfma_bf16(as_bf16x8<KVT>(kr[t][kk]), qb[kk], acc);
+                acc = mfma_bf16(k_operand(t, kk), qb[kk], acc);
             const bool tv = (t ? cpg1 : cpg0) >= 0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -698,7 +707,7 @@ decode_persistent_kernel(PartialArgs a)
             ok = ok && fixed_shift_row(q_row_norm<KK>(qb), ci.kb, fabsf(scale2), C, gate, m_fix);
             fixed = __all(ok);
         }
-        if (more) {
+        if (!RM && more) {
             issue_k(cur, c, pg0, pg1);
             if (c == cur.nchunk - 1)
                 prepare_next();
@@ -714,7 +723,7 @@ decode_persistent_kernel(PartialArgs a)
         }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-            const u32x4 va = vt_operand<DT>(vt_lane, dt);
+            const u32x4 va = v_operand(dt);
             o[dt] = mfma_bf16(va, ph, o[dt]);
             if constexpr (PVS)
                 o[dt] = mfma_bf16(va, pl, o[dt]);

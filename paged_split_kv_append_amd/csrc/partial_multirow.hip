@@ -223,9 +223,9 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
             if (x >= per)                      // (never taken when K and V widths match)
                 break;
             if constexpr (BF)
-                rg.r16[x] = nbx_buffer_load_b128(rs, role_lane + x * 32 * ESZ, 0, 0);
+                rg.r16[x] = nbx_buffer_load_b128(rs, role_lane + x * 32 * ESZ, 0, kStreamAux);
             else
-                rg.r8[x] = nbx_buffer_load_b64(rs, role_lane + x * 32 * ESZ, 0, 0);
+                rg.r8[x] = nbx_buffer_load_b64(rs, role_lane + x * 32 * ESZ, 0, kStreamAux);
         }
     };
     // this wave's pieces of a chunk, landed in registers, into an LDS buffer
