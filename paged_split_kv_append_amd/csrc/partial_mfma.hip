@@ -398,12 +398,16 @@ decode_persistent_kernel(PartialArgs a)
         carry = __shfl(incl[t], 63, 64);
     }
     const int N = carry;
+    // value of wave-uniform sequence b in a lane table (lane reads of the
+    // table registers themselves, valid whatever lanes are active)
     auto lane_val = [&](const int (&arr)[NB], int b) {
-        int v = arr[0];
+        int v = __builtin_amdgcn_readlane(arr[0], b & 63);
 #pragma unroll
-        for (int t = 1; t < NB; ++t)
-            v = (b >> 6) == t ? arr[t] : v;
-        return __builtin_amdgcn_readlane(v, b & 63);
+        for (int t = 1; t < NB; ++t) {
+            const int x = __builtin_amdgcn_readlane(arr[t], b & 63);
+            v = (b >> 6) == t ? x : v;
+        }
+        return v;
     };
 
     // splits without keys: m = -inf, l = 0 for their rows
@@ -469,19 +473,24 @@ decode_persistent_kernel(PartialArgs a)
     };
     // Fused append: the new positions L - n_new .. L - 1 that fall in the item
     // are written to the pools (the conversions of the append kernel) before
-    // any load of the item is issued.  Only this wave reads the item's tiles,
-    // and a wave's memory operations are performed in order, so its later
-    // tile loads see the new rows.
+    // any load of the item is issued.  The item of the last split also takes
+    // the positions at or past NS * S that no item covers (a length the split
+    // plan does not reach, flagged above); a sequence longer than its
+    // block-table row gets none (the separate append skips it the same way).
+    // Only this wave reads the item's tiles, and a wave's memory operations
+    // are performed in order, so its later tile loads see the new rows.
     // `pg` holds the page ids of the item's first 32 chunks (item_pages(it, 0)).
     // With bounds, each written row raises its page's bound and the item's.
     auto append_item = [&](Item &it, int pg) {
         if constexpr (FA) {
-            const int first = it.L - a.n_new;
-            const int lo = max(it.j0, max(first, 0)), hi = min(it.j0 + S, it.L);
+            const int Lw = a.seq_lens[it.b];   // as given (it.L is clamped to the row)
+            const int first = Lw - a.n_new;
+            const int lo = max(it.j0, max(first, 0));
+            const int hi = Lw > cap ? lo : it.s == NS - 1 ? Lw : min(it.j0 + S, Lw);
             for (int p = lo; p < hi; ++p) {
                 const int tl = (p - it.j0) >> 4;           // tile of p within the item
-                const int page = tl < 64 ? __builtin_amdgcn_readlane(pg, tl)
-                                         : tile_page(a, it.b, p, hi, lane == 0);
+                const int page = tl < 64 && p < it.jend ? __builtin_amdgcn_readlane(pg, tl)
+                                                        : tile_page(a, it.b, p, hi, lane == 0);
                 if (page < 0)
                     continue;
                 const int64_t src = ((int64_t)it.b * a.n_new + (p - first)) * H + it.gk;

@@ -35,7 +35,10 @@ namespace {
 // counter read 28% of the LDS-active cycles, and the prompt chunk took 9% longer.)
 // Within each phase the LDS operand reads run ahead of the products that use
 // them (schedule_reads_ahead): K one k-step ahead, V four operands ahead.
-template <int D, int DV, int KVT, bool PVS, int NT, int NK, int NSET>
+// NTL: the K/V loads are marked non-temporal (one row block per split: no
+// other workgroup reads the same tiles); with several row blocks they stay
+// cacheable, since the row blocks of a split read its tiles from the L2.
+template <int D, int DV, int KVT, bool PVS, int NT, int NK, int NSET, bool NTL>
 __global__ void __launch_bounds__(512)
 multirow_mfma_kernel(PartialArgs a, int row_blocks)
 {
@@ -223,9 +226,9 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
             if (x >= per)                      // (never taken when K and V widths match)
                 break;
             if constexpr (BF)
-                rg.r16[x] = nbx_buffer_load_b128(rs, role_lane + x * 32 * ESZ, 0, kStreamAux);
+                rg.r16[x] = nbx_buffer_load_b128(rs, role_lane + x * 32 * ESZ, 0, NTL ? kStreamAux : 0);
             else
-                rg.r8[x] = nbx_buffer_load_b64(rs, role_lane + x * 32 * ESZ, 0, kStreamAux);
+                rg.r8[x] = nbx_buffer_load_b64(rs, role_lane + x * 32 * ESZ, 0, NTL ? kStreamAux : 0);
         }
     };
     // this wave's pieces of a chunk, landed in registers, into an LDS buffer
@@ -394,14 +397,18 @@ hipError_t launch_mr(const PartialArgs &a, hipStream_t stream)
     if (!grid_fits(blocks, 512))
         return hipErrorInvalidConfiguration;
     if constexpr (D <= 128) {                 // two row tiles per wave only below D = 256
-        if (nt == 2) {
-            hipLaunchKernelGGL((multirow_mfma_kernel<D, DV, KVT, PVS, 2, kMrNK, kMrNSet>),
+        if (nt == 2) {                         // (more than 128 rows: several row blocks)
+            hipLaunchKernelGGL((multirow_mfma_kernel<D, DV, KVT, PVS, 2, kMrNK, kMrNSet, false>),
                                dim3((unsigned)blocks), dim3(512), 0, stream, a, row_blocks);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((multirow_mfma_kernel<D, DV, KVT, PVS, 1, kMrNK, kMrNSet>),
-                       dim3((unsigned)blocks), dim3(512), 0, stream, a, row_blocks);
+    if (row_blocks == 1)
+        hipLaunchKernelGGL((multirow_mfma_kernel<D, DV, KVT, PVS, 1, kMrNK, kMrNSet, true>),
+                           dim3((unsigned)blocks), dim3(512), 0, stream, a, row_blocks);
+    else
+        hipLaunchKernelGGL((multirow_mfma_kernel<D, DV, KVT, PVS, 1, kMrNK, kMrNSet, false>),
+                           dim3((unsigned)blocks), dim3(512), 0, stream, a, row_blocks);
     return hipGetLastError();
 }
 

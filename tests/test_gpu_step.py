@@ -283,6 +283,63 @@ def test_step_sequence_shorter_than_new_tokens_is_flagged():
     assert max_abs(out, ref) <= TOL["bf16"]
 
 
+def _two_call_reference(case, lens, slots, n_split, split):
+    """The step's work as separate calls: nbx_paged_kv_append at `slots` (-1:
+    skipped), then nbx_paged_decode with the device lengths `lens`."""
+    dref = DevCase(case)
+    dref.lens = torch.as_tensor(np.asarray(lens, dtype=np.int32)).to(dref.q.device)
+    kp, vp = dref.pools()
+    nb.nbx_paged_kv_append(dref.new_k, dref.new_v, kp, vp,
+                           torch.as_tensor(np.asarray(slots, dtype=np.int32)).to(dref.q.device),
+                           dev_err=dref.err)
+    return dref, dref.decode(n_split, split)
+
+
+def test_step_sequence_past_its_block_table_row_equals_two_call_path():
+    """A length past max_pages * page_tokens: the single-launch step writes no
+    new row for that sequence (the separate append skips it and flags it) and
+    reads the sequence clamped to its block-table row, exactly as the two
+    separate calls do."""
+    case = synth.make_case(2, seed=61, batch=5, lens=("uniform", 40, 300))
+    cap = case.max_pages * case.page_tokens
+    lens = case.seq_lens.copy()
+    lens[2] = cap + 1
+    slots = case.slot_mapping.copy()
+    slots[2] = -1                              # the two-call path's append skips it too
+    n_split, split = 8, 48                     # covers the whole row (8 * 48 >= cap)
+    assert n_split * split >= cap
+    print(f"step with seq_len {cap + 1} past the row of {cap}", flush=True)
+    dc = DevCase(case)
+    dc.lens = torch.as_tensor(lens).to(dc.q.device)
+    out = dc.step(n_split=n_split, split_size=split)
+    dref, ref = _two_call_reference(case, lens, slots, n_split, split)
+    torch.cuda.synchronize()
+    assert dc.err_bits() & nb.DEVERR_SEQ_RANGE
+    assert dc.err_bits() == dref.err_bits()
+    assert np.array_equal(_pool_bits(dc.k), _pool_bits(dref.k))
+    assert np.array_equal(_pool_bits(dc.v), _pool_bits(dref.v))
+    assert torch.equal(out, ref)
+
+
+def test_step_new_position_past_the_split_cover_equals_two_call_path():
+    """Splits that cover fewer positions than some sequences hold (flagged): the
+    new rows past n_split * split_size are still written, as the separate append
+    writes them, and the read covers the same positions on both paths."""
+    case = synth.make_case(2, seed=62, batch=6, lens=("uniform", 100, 300))
+    n_split, split = 2, 64
+    assert int(case.seq_lens.max()) > n_split * split
+    print(f"step with cover {n_split * split} < longest {int(case.seq_lens.max())}", flush=True)
+    dc = DevCase(case)
+    out = dc.step(n_split=n_split, split_size=split)
+    dref, ref = _two_call_reference(case, case.seq_lens, case.slot_mapping, n_split, split)
+    torch.cuda.synchronize()
+    assert dc.err_bits() & nb.DEVERR_SEQ_RANGE
+    assert dc.err_bits() == dref.err_bits()
+    assert np.array_equal(_pool_bits(dc.k), _pool_bits(dref.k))
+    assert np.array_equal(_pool_bits(dc.v), _pool_bits(dref.v))
+    assert torch.equal(out, ref)
+
+
 @pytest.mark.parametrize("workload", [2, 5])
 def test_step_full_size_against_oracle(workload):
     case = synth.make_case(workload)
