@@ -69,7 +69,10 @@ typedef enum {
     NBX_ERR_UNSUPPORTED = -6,   /* valid request this build does not implement, or
                                    whose grid exceeds the 2^32 work-items of one
                                    dispatch */
-    NBX_ERR_LAUNCH = -7         /* the HIP runtime refused a kernel launch */
+    NBX_ERR_LAUNCH = -7,        /* the HIP runtime refused a kernel launch */
+    NBX_ERR_SCRATCH_LIMIT = -8  /* the partials of the request need more than the
+                                   library's static scratch holds
+                                   (NBX_STEP_SCRATCH_BYTES) */
 } nbx_status;
 
 /* device-side data error bits OR-ed into *dev_err */
@@ -360,6 +363,41 @@ int nbx_paged_decode_step(const void *q, int32_t q_dtype, int32_t batch, int32_t
                           int32_t split_size, int32_t n_split, void *workspace,
                           size_t workspace_bytes, void *out, int32_t out_dtype, int32_t *dev_err,
                           hipStream_t stream);
+
+/* Bytes of the device scratch of nbx_paged_decode_step_noalloc (32 MiB). */
+#define NBX_STEP_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * nbx_paged_decode_step_noalloc - nbx_paged_decode_step for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same append, partial and
+ * merge, with the split partials kept in a static device array of the
+ * library, NBX_STEP_SCRATCH_BYTES per GPU, instead of a caller workspace.
+ * The call itself allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine); each GPU the library runs on holds the array from the
+ * loading of the library's code on it until the process ends.
+ *
+ *   out    required (NBX_ERR_NULL_PTR if null): the partials are internal.
+ * Other arguments, errors and results as for nbx_paged_decode_step.  A request
+ * whose partials, nbx_paged_decode_workspace_bytes(batch * q_heads * q_rows,
+ * n_split, Dv), exceed NBX_STEP_SCRATCH_BYTES returns NBX_ERR_SCRATCH_LIMIT
+ * before any launch (1024 rows at Dv = 128 take up to 63 splits).  The first
+ * call on a device looks the array's address up (hipGetSymbolAddress) with
+ * that device current; NBX_ERR_LAUNCH if that fails.
+ *
+ * Every call on one GPU uses that GPU's one array, which keeps the last
+ * call's partials: calls that overlap on one GPU (on different streams, or
+ * from different threads without ordering) race and give wrong results.
+ * Calls on one stream run in turn and are safe.
+ */
+int nbx_paged_decode_step_noalloc(const void *q, int32_t q_dtype, int32_t batch, int32_t q_heads,
+                                  int32_t q_rows, int32_t causal, const void *new_k,
+                                  const void *new_v, int32_t new_dtype, int32_t n_new,
+                                  const nbx_kv_pool *k_pool, const nbx_kv_pool *v_pool,
+                                  const int32_t *block_table, int32_t max_pages,
+                                  const int32_t *seq_lens, float scale, int32_t split_size,
+                                  int32_t n_split, void *out, int32_t out_dtype, int32_t *dev_err,
+                                  hipStream_t stream);
 
 /*
  * nbx_paged_lens_advance - seq_lens[b] += n for 0 <= b < batch, on the device

@@ -22,6 +22,8 @@ HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__fil
                            "include", "nbx_paged.h")
 
 NBX_F32, NBX_BF16, NBX_FP8_E4M3 = 0, 1, 2
+NBX_ERR_SCRATCH_LIMIT = -8
+STEP_SCRATCH_BYTES = 32 << 20              # NBX_STEP_SCRATCH_BYTES
 DEVERR_SLOT_RANGE, DEVERR_PAGE_RANGE, DEVERR_SEQ_RANGE = 0x1, 0x2, 0x4
 
 
@@ -85,6 +87,10 @@ def load_library():
                                                   PP, P, I32, P, F, I32, I32, P, ctypes.c_size_t,
                                                   P, I32, P, P]
             lib.nbx_paged_decode_step.restype = ctypes.c_int
+            lib.nbx_paged_decode_step_noalloc.argtypes = [P, I32, I32, I32, I32, I32, P, P, I32,
+                                                          I32, PP, PP, P, I32, P, F, I32, I32, P,
+                                                          I32, P, P]
+            lib.nbx_paged_decode_step_noalloc.restype = ctypes.c_int
             lib.nbx_paged_lens_advance.argtypes = [P, I32, I32, P]
             lib.nbx_paged_lens_advance.restype = ctypes.c_int
             lib.nbx_paged_decode_partial_windows.argtypes = [P, I32, I32, I32, I32, P, I32, PP, PP,
@@ -318,6 +324,20 @@ def nbx_paged_decode(q, k_pool: KVPool, v_pool: KVPool, block_table, seq_lens, s
     _check(st, "nbx_paged_decode")
 
 
+def _new_rows(new_k, new_v, B, k_pool, D, Dv):
+    """(n_new, dtype code) of a step's new rows (0, 0 without them), shapes checked."""
+    if new_k is None:
+        return 0, 0
+    if new_v is None or new_k.shape[:3] != new_v.shape[:3] or new_k.dtype != new_v.dtype:
+        raise ValueError("new_k and new_v must match")
+    if new_k.dim() != 4 or new_k.shape[0] != B or new_k.shape[2] != k_pool.data.shape[1] \
+            or new_k.shape[3] != D or new_v.shape[3] != Dv \
+            or not (new_k.is_contiguous() and new_v.is_contiguous()):
+        raise ValueError("new_k / new_v must be contiguous [batch, n_new, kv_heads, "
+                         "head_dim / v_head_dim]")
+    return new_k.shape[1], _dtype_code(new_k)
+
+
 def nbx_paged_decode_step(q, k_pool: KVPool, v_pool: KVPool, block_table, seq_lens, scale: float,
                           split_size: int, n_split: int, workspace, out, new_k=None, new_v=None,
                           causal: bool = False, dev_err=None, stream=None):
@@ -331,16 +351,7 @@ def nbx_paged_decode_step(q, k_pool: KVPool, v_pool: KVPool, block_table, seq_le
     Dv = v_pool.data.shape[3]
     if out is not None and (out.numel() != B * Hq * W * Dv or not out.is_contiguous()):
         raise ValueError("out must be contiguous [batch, q_heads, q_rows, v_head_dim]")
-    n_new, new_dt = 0, 0
-    if new_k is not None:
-        if new_v is None or new_k.shape[:3] != new_v.shape[:3] or new_k.dtype != new_v.dtype:
-            raise ValueError("new_k and new_v must match")
-        if new_k.dim() != 4 or new_k.shape[0] != B or new_k.shape[2] != k_pool.data.shape[1] \
-                or new_k.shape[3] != D or new_v.shape[3] != Dv \
-                or not (new_k.is_contiguous() and new_v.is_contiguous()):
-            raise ValueError("new_k / new_v must be contiguous [batch, n_new, kv_heads, "
-                             "head_dim / v_head_dim]")
-        n_new, new_dt = new_k.shape[1], _dtype_code(new_k)
+    n_new, new_dt = _new_rows(new_k, new_v, B, k_pool, D, Dv)
     st = load_library().nbx_paged_decode_step(
         _ptr(q), _dtype_code(q), B, Hq, W, int(bool(causal)), _ptr(new_k), _ptr(new_v), new_dt,
         n_new, ctypes.byref(kd), ctypes.byref(vd), _ptr(block_table), block_table.shape[1],
@@ -348,6 +359,25 @@ def nbx_paged_decode_step(q, k_pool: KVPool, v_pool: KVPool, block_table, seq_le
         _workspace_bytes(workspace), _ptr(out),
         _dtype_code(out) if out is not None else 0, _dev_err(dev_err), _stream(stream))
     _check(st, "nbx_paged_decode_step")
+
+
+def nbx_paged_decode_step_noalloc(q, k_pool: KVPool, v_pool: KVPool, block_table, seq_lens,
+                                  scale: float, split_size: int, n_split: int, out, new_k=None,
+                                  new_v=None, causal: bool = False, dev_err=None, stream=None):
+    """nbx_paged_decode_step with the partials in the library's static device scratch
+    (no workspace argument; the call allocates nothing).  ``out`` is required."""
+    kd, vd = _decode_common(q, k_pool, v_pool, block_table, seq_lens)
+    B, Hq, W, D = q.shape
+    Dv = v_pool.data.shape[3]
+    if out is None or out.numel() != B * Hq * W * Dv or not out.is_contiguous():
+        raise ValueError("out must be contiguous [batch, q_heads, q_rows, v_head_dim]")
+    n_new, new_dt = _new_rows(new_k, new_v, B, k_pool, D, Dv)
+    st = load_library().nbx_paged_decode_step_noalloc(
+        _ptr(q), _dtype_code(q), B, Hq, W, int(bool(causal)), _ptr(new_k), _ptr(new_v), new_dt,
+        n_new, ctypes.byref(kd), ctypes.byref(vd), _ptr(block_table), block_table.shape[1],
+        _ptr(seq_lens), float(scale), int(split_size), int(n_split), _ptr(out), _dtype_code(out),
+        _dev_err(dev_err), _stream(stream))
+    _check(st, "nbx_paged_decode_step_noalloc")
 
 
 def workspace_partials(workspace, rows: int, n_split: int, head_dim: int):

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "kernels.h"
 #include "nbx_paged.h"
 
@@ -92,6 +94,7 @@ const char *nbx_status_str(int status)
     case NBX_ERR_WORKSPACE: return "workspace too small or misaligned";
     case NBX_ERR_UNSUPPORTED: return "request not supported by this build";
     case NBX_ERR_LAUNCH: return "kernel launch failed";
+    case NBX_ERR_SCRATCH_LIMIT: return "request needs more than the static scratch holds";
     default: return "unknown status";
     }
 }
@@ -495,14 +498,19 @@ int nbx_paged_decode(const void *q, int32_t q_dtype, int32_t batch, int32_t q_he
                                   stream);
 }
 
-int nbx_paged_decode_step(const void *q, int32_t q_dtype, int32_t batch, int32_t q_heads,
-                          int32_t q_rows, int32_t causal, const void *new_k, const void *new_v,
-                          int32_t new_dtype, int32_t n_new, const nbx_kv_pool *k_pool,
-                          const nbx_kv_pool *v_pool, const int32_t *block_table,
-                          int32_t max_pages, const int32_t *seq_lens, float scale,
-                          int32_t split_size, int32_t n_split, void *workspace,
-                          size_t workspace_bytes, void *out, int32_t out_dtype, int32_t *dev_err,
-                          hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+// The step with the partials in `workspace`; `small_ws` is the status of a
+// workspace that is too small (the caller's, or the static scratch's limit).
+int decode_step(const void *q, int32_t q_dtype, int32_t batch, int32_t q_heads, int32_t q_rows,
+                int32_t causal, const void *new_k, const void *new_v, int32_t new_dtype,
+                int32_t n_new, const nbx_kv_pool *k_pool, const nbx_kv_pool *v_pool,
+                const int32_t *block_table, int32_t max_pages, const int32_t *seq_lens,
+                float scale, int32_t split_size, int32_t n_split, void *workspace,
+                size_t workspace_bytes, int small_ws, void *out, int32_t out_dtype,
+                int32_t *dev_err, hipStream_t stream)
 {
     int st = validate_partial(q, q_dtype, batch, q_heads, q_rows, causal, k_pool, v_pool,
                               block_table, max_pages, seq_lens, scale, split_size, n_split);
@@ -532,8 +540,10 @@ int nbx_paged_decode_step(const void *q, int32_t q_dtype, int32_t batch, int32_t
     const int64_t rows = (int64_t)batch * q_heads * q_rows;
     const int32_t D = k_pool->head_dim, Dv = v_pool->head_dim;
     const size_t need = nbx_paged_decode_workspace_bytes(rows, n_split, Dv);
-    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
+    if (!workspace || ((uintptr_t)workspace & 255u))
         return NBX_ERR_WORKSPACE;
+    if (workspace_bytes < need)
+        return small_ws;
     char *ws = (char *)workspace;
     float *o_part = (float *)ws;
     float *m_part = (float *)(ws + round256((size_t)rows * n_split * Dv * sizeof(float)));
@@ -596,6 +606,81 @@ int nbx_paged_decode_step(const void *q, int32_t q_dtype, int32_t batch, int32_t
         return NBX_OK;                         // partials only, left in the workspace
     nbx::MergeArgs m{o_part, m_part, l_part, rows, n_split, Dv, out, out_dtype};
     return to_status(nbx::launch_merge(m, stream));
+}
+
+// Partials of nbx_paged_decode_step_noalloc.  Host code uses the address that
+// hipGetSymbolAddress gives for the current device (scratch_on_device), never
+// the name, which on the host side is no device address.
+static __device__ __align__(256) uint8_t scratch[NBX_STEP_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<uintptr_t> scratch_addr[kMaxScratchDevices];
+
+// The current device's copy of `scratch`, looked up once per device (with that
+// device current); null if the lookup fails.  Concurrent first calls may both
+// look it up: they store the same address.
+void *scratch_on_device()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices)
+        return nullptr;
+    uintptr_t p = scratch_addr[dev].load(std::memory_order_acquire);
+    if (p == 0) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+            return nullptr;
+        p = (uintptr_t)ptr;
+        scratch_addr[dev].store(p, std::memory_order_release);
+    }
+    return (void *)p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nbx_paged_decode_step(const void *q, int32_t q_dtype, int32_t batch, int32_t q_heads,
+                          int32_t q_rows, int32_t causal, const void *new_k, const void *new_v,
+                          int32_t new_dtype, int32_t n_new, const nbx_kv_pool *k_pool,
+                          const nbx_kv_pool *v_pool, const int32_t *block_table,
+                          int32_t max_pages, const int32_t *seq_lens, float scale,
+                          int32_t split_size, int32_t n_split, void *workspace,
+                          size_t workspace_bytes, void *out, int32_t out_dtype, int32_t *dev_err,
+                          hipStream_t stream)
+{
+    return decode_step(q, q_dtype, batch, q_heads, q_rows, causal, new_k, new_v, new_dtype, n_new,
+                       k_pool, v_pool, block_table, max_pages, seq_lens, scale, split_size,
+                       n_split, workspace, workspace_bytes, NBX_ERR_WORKSPACE, out, out_dtype,
+                       dev_err, stream);
+}
+
+int nbx_paged_decode_step_noalloc(const void *q, int32_t q_dtype, int32_t batch, int32_t q_heads,
+                                  int32_t q_rows, int32_t causal, const void *new_k,
+                                  const void *new_v, int32_t new_dtype, int32_t n_new,
+                                  const nbx_kv_pool *k_pool, const nbx_kv_pool *v_pool,
+                                  const int32_t *block_table, int32_t max_pages,
+                                  const int32_t *seq_lens, float scale, int32_t split_size,
+                                  int32_t n_split, void *out, int32_t out_dtype, int32_t *dev_err,
+                                  hipStream_t stream)
+{
+    if (!out)
+        return NBX_ERR_NULL_PTR;
+    // the size limit is checked on the validated shape, before the device is touched
+    int st = validate_partial(q, q_dtype, batch, q_heads, q_rows, causal, k_pool, v_pool,
+                              block_table, max_pages, seq_lens, scale, split_size, n_split);
+    if (st != NBX_OK)
+        return st;
+    const int64_t rows = (int64_t)batch * q_heads * q_rows;
+    if (rows > 0 &&
+        nbx_paged_decode_workspace_bytes(rows, n_split, v_pool->head_dim) > NBX_STEP_SCRATCH_BYTES)
+        return NBX_ERR_SCRATCH_LIMIT;
+    void *ws = rows > 0 ? scratch_on_device() : nullptr;   // batch 0: nothing to do
+    if (rows > 0 && !ws)
+        return NBX_ERR_LAUNCH;
+    return decode_step(q, q_dtype, batch, q_heads, q_rows, causal, new_k, new_v, new_dtype, n_new,
+                       k_pool, v_pool, block_table, max_pages, seq_lens, scale, split_size,
+                       n_split, ws, NBX_STEP_SCRATCH_BYTES, NBX_ERR_SCRATCH_LIMIT, out, out_dtype,
+                       dev_err, stream);
 }
 
 }  // extern "C"

@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for st in range(0, -8, -1):
+    for st in range(0, -9, -1):
         s = nb.status_str(st)
         assert s and s != "unknown status"
     assert nb.status_str(-99) == "unknown status"
@@ -218,6 +218,22 @@ def test_step_validation(lib):
     assert call(ws=None) == -5
     assert call(nbytes=need - 1) == -5
     assert call(ws=FAKE + 16) == -5
+
+
+def test_noalloc_step_validation(lib):
+    """Refusals of the no-allocation step, all on the host: a null output (the
+    partials stay internal) and partials larger than the static scratch."""
+    k, v = pool(), pool()
+
+    def call(batch=2, n_split=2, out=FAKE):
+        return lib.nbx_paged_decode_step_noalloc(
+            FAKE, 1, batch, 4, 1, 0, FAKE, FAKE, 1, 1, ctypes.byref(k), ctypes.byref(v), FAKE,
+            4, FAKE, 0.1, 16, n_split, out, 0, None, None)
+    assert call(out=None) == -1
+    # 4096 rows x 64 splits x 128 floats = 128 MiB of partials > 32 MiB
+    assert nb.nbx_paged_decode_workspace_bytes(4096, 64, 128) > nb.STEP_SCRATCH_BYTES
+    assert call(batch=1024, n_split=64) == nb.NBX_ERR_SCRATCH_LIMIT
+    assert call(batch=0, n_split=64) == 0      # nothing to do, no device needed
 
 
 def test_lens_advance_validation(lib):
