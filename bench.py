@@ -9,7 +9,9 @@ tensors resident in HBM before timing starts.  Before every timed step a
 stream the kernels run on.
 
 Prints one JSON line: value = algorithmic K/V bytes / step time (GB/s),
-plus the roofline of the dominant kernel (the split partial) and the oracle
+plus the roofline of the dominant kernel (the split partial), the practical
+read ceiling (the same bytes read as a plain stream and as random 4 KB blocks
+by the probes of libnbx_read_ceiling.so, after the same flush) and the oracle
 timed on the host cores over a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -213,6 +215,34 @@ def summarize_trace(trace_dir: str):
     return "\n".join(out)
 
 
+def summarize_ceiling(trace_dir: str, workload: int):
+    """Kernel-trace times of the read-ceiling probe in a rocprofv3 --kernel-trace
+    run of bench.py: its dispatches in launch order, in runs of one grid size
+    (address order at 1024, 2048, 4096 workgroups, then random order at the same
+    grids), each run's first dispatch left out as its warm-up."""
+    import csv
+    import glob
+    from paged_split_kv_append_amd import synth
+    nbytes = -(-synth.make_case(workload, poison=False).kv_bytes() // 4096) * 4096
+    fn = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)[0]
+    rows = [r for r in csv.DictReader(open(fn)) if "block_read_kernel" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    runs = []
+    for r in rows:
+        grid = int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"])
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        if not runs or runs[-1][0] != grid:
+            runs.append((grid, []))
+        runs[-1][1].append(us)
+    out = [f"{'order':>10} {'workgroups':>10} {'dispatches':>10} {'median_us':>10} {'GB/s':>8}"]
+    for i, (grid, us) in enumerate(runs):
+        order = "address" if i < len(runs) // 2 else "random"
+        med = float(np.median(us[1:] if len(us) > 1 else us))
+        out.append(f"{order:>10} {grid:>10} {len(us) - 1:>10} {med:>10.2f} "
+                   f"{nbytes / (med * 1e-6) / 1e9:>8.1f}")
+    return "\n".join(out)
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -273,6 +303,62 @@ def cpu_baseline(case, budget_s: float = 10.0):
     }
 
 
+def read_ceiling(kv_bytes: int, flush_caches, stream_ptr: int, reps: int = 15):
+    """The practical ceiling of a read of kv_bytes on this GPU: the same bytes
+    (rounded up to 4 KB) read by one probe kernel as 4 KB blocks, one wave per
+    block, in address order (a plain stream) and in a seeded random order (the
+    decode reads 16-position pages of one KV head, 4 KB at D = 128 bf16), after
+    the same cache flush as the step and timed with HIP events; for each order
+    the best median GB/s over grids of 1024, 2048 and 4096 workgroups."""
+    import ctypes
+
+    import torch
+    path = os.path.join(ROOT, "paged_split_kv_append_amd", "libnbx_read_ceiling.so")
+    if not os.path.exists(path):
+        raise FileNotFoundError(f"{path} is missing: build it with "
+                                "`python -m paged_split_kv_append_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32 = ctypes.c_void_p, ctypes.c_int32
+    lib.nbx_ceiling_block_read.argtypes = [P, P, I32, I32, P, P]
+    dev = torch.device("cuda:0")
+    nblocks = -(-kv_bytes // 4096)
+    raw = torch.ones(nblocks * 4096 + 4096, dtype=torch.uint8, device=dev)
+    base = (raw.data_ptr() + 4095) // 4096 * 4096          # 4 KB aligned, nblocks * 4096 bytes
+    gen = torch.Generator().manual_seed(4096)
+    orders = {"stream": torch.arange(nblocks, dtype=torch.int32, device=dev),
+              "random_4k": torch.randperm(nblocks, generator=gen).to(torch.int32).to(dev)}
+    grids = (1024, 2048, 4096)
+    sink = torch.zeros(max(grids) * 256, dtype=torch.int32, device=dev)
+
+    def run(order, wgs):
+        st = lib.nbx_ceiling_block_read(P(base), P(order.data_ptr()), nblocks, wgs,
+                                        P(sink.data_ptr()), P(stream_ptr))
+        if st != 0:
+            raise RuntimeError(f"read-ceiling launch: status {st}")
+
+    res = {"bytes": nblocks * 4096, "reps": reps, "timing": "HIP events around the probe "
+           "launch after the flush, median of reps, best grid"}
+    for kind, order in orders.items():
+        best = None
+        for wgs in grids:
+            run(order, wgs)
+            evs = [(HipEvent(), HipEvent()) for _ in range(reps)]
+            for a, b in evs:
+                flush_caches()
+                a.record(stream_ptr)
+                run(order, wgs)
+                b.record(stream_ptr)
+            torch.cuda.synchronize()
+            med = float(np.median([a.elapsed_ms(b) for a, b in evs]))
+            if best is None or med < best[0]:
+                best = (med, wgs)
+        res[kind + "_read_gbs"] = round(nblocks * 4096 / (best[0] * 1e-3) / 1e9, 1)
+        res[kind + "_read_us_median"] = round(best[0] * 1e3, 2)
+        res[kind + "_workgroups"] = best[1]
+    del raw, orders, sink
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -291,14 +377,22 @@ def main():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a known-size "
                          "reference for the profiler's byte counters)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the read-ceiling probes (plain stream and random 4 KB blocks)")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="print the kernel table of a rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--summarize-ceiling", metavar="DIR",
+                    help="print the read-ceiling probe's kernel times from a rocprofv3 "
+                         "--kernel-trace run of bench.py (of --workload)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the split partial's traffic from FETCH_SIZE / WRITE_SIZE runs "
                          "made with --copy-mib")
     args = ap.parse_args()
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace))
+        return
+    if args.summarize_ceiling:
+        print(summarize_ceiling(args.summarize_ceiling, args.workload))
         return
     if args.summarize_counters:
         print(summarize_counters(*args.summarize_counters, args.copy_mib or 256, args.workload))
@@ -445,7 +539,8 @@ def main():
     mfma_info = None
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": kernel_name, "us_per_launch": round(t_part * 1e6, 2)}
+                "kernel": kernel_name, "us_per_launch": round(t_part * 1e6, 2),
+                "us_per_launch_median": round(float(np.median(part_ms)) * 1e3, 2)}
     if case.kv_dtype in MFMA_PEAK_TFLOPS and case.q_rows > 1:
         fl = flops_of(case)
         tflops = fl / t_part / 1e12
@@ -484,7 +579,9 @@ def main():
                    "softmax": ("fixed shift from per-page K/V bounds" if args.bounds
                                else "running maximum"),
                    "seed": args.seed if args.seed is not None else args.workload},
+        "ms_per_step_median": round(float(np.median(step_ms)), 5),
         "us_per_step": round(float(step_ms.mean()) * 1e3, 2),
+        "us_per_step_median": round(float(np.median(step_ms)) * 1e3, 2),
         "us_per_step_p10_p90": [round(float(np.percentile(step_ms, 10)) * 1e3, 2),
                                 round(float(np.percentile(step_ms, 90)) * 1e3, 2)],
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -493,6 +590,11 @@ def main():
     }
     if mfma_info is not None:
         res["mfma"] = mfma_info
+    if not args.no_ceiling:
+        ceil = read_ceiling(kv, flush_caches, stream_ptr)
+        ceil["partial_frac_of_random_4k"] = round(achieved / ceil["random_4k_read_gbs"], 4)
+        ceil["step_frac_of_random_4k"] = round(value / ceil["random_4k_read_gbs"], 4)
+        res["practical_ceiling"] = ceil
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(res), flush=True)

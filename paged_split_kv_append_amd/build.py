@@ -2,7 +2,9 @@
 
 Each ``csrc/*.hip`` file is compiled to an object under ``_build/`` and the
 objects are linked into ``paged_split_kv_append_amd/libnbx_paged.so`` next to
-this file.  ``python -m paged_split_kv_append_amd.build`` runs it.
+this file.  The read-ceiling probes the benchmark times beside the decode
+(``ceiling/read_ceiling.hip``) go to a library of their own,
+``libnbx_read_ceiling.so``.  ``python -m paged_split_kv_append_amd.build`` runs it.
 """
 from __future__ import annotations
 
@@ -19,6 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libnbx_paged.so")
+CEILING_SRC = os.path.join(PKG, "ceiling", "read_ceiling.hip")
+CEILING_LIB = os.path.join(PKG, "libnbx_read_ceiling.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -53,8 +57,14 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    tmp = CEILING_LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *COMMON, "-shared", CEILING_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {CEILING_SRC}:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, CEILING_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CEILING_LIB}")
     return LIB
 
 

@@ -280,7 +280,26 @@ def test_batch_beyond_the_persistent_table(kv_dtype, split):
 
 # ------------------------------------------------------------------ full sizes
 
-FULL_ROWS = {2: None, 5: None, 3: [(0, 48), (1488, 1536)], 4: [(0, 32), (3040, 3072)]}
+def _full_rows(case):
+    """Row ranges compared with the oracle at full size: every row of the decode
+    shapes; for the 16-row verify window, the rows of every query head of KV
+    head g in sequence g (all four KV heads, all four sequences); for the
+    128-row prompt chunk, the first and last 16-row tile of every query head
+    (every 128-row block of every KV head)."""
+    if case.q_rows == 1:
+        return [(0, case.rows)]
+    G = case.q_heads // case.kv_heads
+    W = case.q_rows
+    if W == 16:
+        return [(((g % case.batch) * case.q_heads + g * G) * W,
+                 ((g % case.batch) * case.q_heads + (g + 1) * G) * W)
+                for g in range(case.kv_heads)]
+    out = []
+    for b in range(case.batch):
+        for h in range(case.q_heads):
+            r = (b * case.q_heads + h) * W
+            out += [(r, r + 16), (r + W - 16, r + W)]
+    return out
 
 
 @pytest.mark.parametrize("workload", [2, 3, 4, 5])
@@ -298,7 +317,10 @@ def test_full_size_against_oracle(workload):
         kp, vp, _ = oracle.case_append(case)
     else:
         kp, vp = case.k_pool, case.v_pool
-    ranges = FULL_ROWS[workload] or [(0, case.rows)]
+    ranges = _full_rows(case)
+    if workload in (3, 4):                     # every KV head is sampled
+        G, W = case.q_heads // case.kv_heads, case.q_rows
+        assert {(r0 // W % case.q_heads) // G for r0, _ in ranges} == set(range(case.kv_heads))
     for r0, r1 in ranges:
         ref = oracle.attention(case.q, case.q_dtype, kp, vp, case.kv_dtype, case.block_table,
                                case.seq_lens, case.softmax_scale, case.causal, case.k_scale,
@@ -340,6 +362,27 @@ def test_multirow_shapes_match_oracle(name, over):
         out = dc.decode(n_split=n_split, split_size=split)
         torch.cuda.synchronize()
         ref, _, _ = _reference(case, dc)
+        assert dc.err_bits() == 0
+        assert torch.isfinite(out).all()
+        err = max_abs(out, ref)
+        assert err <= TOL[case.kv_dtype], (n_split, split, err)
+
+
+@pytest.mark.parametrize("workload", [3, 4], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("keys", [2100, 9000])
+def test_verify_window_edge_lengths_match_oracle(workload, keys):
+    """16-row causal windows (6 query heads per KV head, D = 256) over 2,100 and
+    9,000 keys: lengths that are not a multiple of the 64-position chunk, read
+    with the planned splits and with one split of the whole sequence (a split
+    whose page ids take more than one batch of tiles)."""
+    case = synth.make_case(workload, seed=70 + keys % 97, batch=2, q_rows=16,
+                           lens=("fixed", keys))
+    print(f"window edge: workload {workload} {case.kv_dtype} keys {keys}", flush=True)
+    dc = DevCase(case)
+    ref, _, _ = _reference(case, dc)
+    for n_split, split in (dc.plan(), (1, -(-keys // 16) * 16)):
+        out = dc.decode(n_split=n_split, split_size=split)
+        torch.cuda.synchronize()
         assert dc.err_bits() == 0
         assert torch.isfinite(out).all()
         err = max_abs(out, ref)

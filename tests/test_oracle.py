@@ -89,6 +89,26 @@ def test_fp8_decode_table_matches_ocp_definition_and_torch():
     assert np.isnan(ours).sum() == 2
 
 
+def test_bf16_decode_table_matches_definition_and_torch():
+    """Every one of the 65,536 bf16 codes: the oracle's value equals torch's
+    bfloat16 -> float64 cast bit for bit (NaN codes both NaN), and spot codes
+    equal the format's definition (the upper 16 bits of a binary32)."""
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.decode_values("bf16", codes)
+    lib = torch.from_numpy(codes.view(np.int16)).view(torch.bfloat16).double().numpy()
+    nan = np.isnan(lib)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan].view(np.uint64), lib[~nan].view(np.uint64))
+    # exponent all ones with a non-zero fraction: 2 * 127 codes
+    assert nan.sum() == 2 * 127
+    assert ours[0x3F80] == 1.0 and ours[0x4000] == 2.0 and ours[0xC040] == -3.0
+    assert ours[0x3F81] == 1.0 + 2.0 ** -7
+    assert ours[0x7F80] == math.inf and ours[0xFF80] == -math.inf
+    assert ours[0x7F7F] == (2.0 - 2.0 ** -7) * 2.0 ** 127
+    assert ours[0x0080] == 2.0 ** -126 and ours[0x0001] == 2.0 ** -133
+    assert ours[0x8000] == 0.0 and math.copysign(1, ours[0x8000]) == -1
+
+
 def _fp32_samples(seed, n=4000):
     rng = np.random.default_rng(seed)
     x = np.concatenate([
