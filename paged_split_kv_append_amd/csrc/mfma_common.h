@@ -33,6 +33,8 @@ __device__ u32x4 nbx_buffer_load_b128(i32x4 rsrc, int voffset, int soffset, int 
     __asm("llvm.amdgcn.raw.buffer.load.v4i32");
 __device__ u32x2 nbx_buffer_load_b64(i32x4 rsrc, int voffset, int soffset, int aux)
     __asm("llvm.amdgcn.raw.buffer.load.v2i32");
+__device__ int nbx_buffer_load_b32(i32x4 rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.i32");
 
 // Cache policy of the K/V tile loads (the aux operand of the buffer loads;
 // bit 1 is gfx950's nt): each K/V byte is read once per launch, so the loads

@@ -350,6 +350,16 @@ decode_persistent_kernel(PartialArgs a)
 
     // sequence table, lane l of block t describing b = 64 t + l: clamped
     // length, splits holding keys, inclusive prefix of item counts
+    // The block table into this XCD's L2 while the lengths are fetched: wave
+    // wv reads 256 bytes of it, the slice wv / 8 (the waves of one XCD are
+    // every eighth), so that the page lookups of the first items, which wait
+    // on the lengths, find it in the cache.  A table larger than (waves / 8) x
+    // 256 bytes is covered from its start; reads past its end return zeros
+    // and touch no memory.
+    const uint64_t bt_bytes = (uint64_t)a.batch * a.max_pages * 4;
+    const int pf = nbx_buffer_load_b32(
+        make_buffer_rsrc(a.block_table, (uint32_t)min(bt_bytes, (uint64_t)0x7FFFFFF0u)),
+        (wv >> 3) * 256 + lane * 4, 0, 0);
     int Lr[NB], Wr[NB], nsr[NB], incl[NB];
     int longest = 1;
 #pragma unroll
@@ -639,6 +649,7 @@ decode_persistent_kernel(PartialArgs a)
 
     int i_item = 0;
     Item cur = make_item(wv);
+    asm volatile("" ::"v"(pf));                // the prefetch has landed (its value is unused)
     int pg_reg = item_pages(cur, 0), pg_next = -1;
     append_item(cur, pg_reg);
     Item nxt = cur;

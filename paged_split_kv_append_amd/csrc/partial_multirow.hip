@@ -352,13 +352,13 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
         refresh(0);
         issue(0, rset[0]);
         land(smem, rset[0]);
-        issue(1, rset[0]);
-        if constexpr (NSET == 2)
-            issue(2, rset[1]);
+#pragma unroll
+        for (int r = 0; r < NSET; ++r)         // chunk k waits in set (k - 1) % NSET
+            issue(1 + r, rset[r]);
         for (int c = 0; c < nchunk; c += NSET) {
-            step(c, rset[0]);                  // lands c + 1, reissues c + 1 + NSET there
-            if constexpr (NSET == 2)
-                step(c + 1, rset[1]);          // lands c + 2, reissues c + 4 there
+#pragma unroll
+            for (int r = 0; r < NSET; ++r)     // lands c + r + 1, reissues c + r + 1 + NSET there
+                step(c + r, rset[r]);
         }
     }
 
@@ -384,7 +384,11 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
 }
 
 // chunks of 2 k-steps (64 positions), one register set in flight
-constexpr int kMrNK = 2, kMrNSet = 1;
+#ifndef NBX_MR_NK
+#define NBX_MR_NK 2
+#define NBX_MR_NSET 1
+#endif
+constexpr int kMrNK = NBX_MR_NK, kMrNSet = NBX_MR_NSET;
 
 template <int D, int DV, int KVT, bool PVS>
 hipError_t launch_mr(const PartialArgs &a, hipStream_t stream)
