@@ -10,6 +10,12 @@
 
 namespace nbx {
 
+// A value every lane of the wave holds alike, moved to a scalar register.
+__device__ __forceinline__ float wave_uniform(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
 __device__ __forceinline__ int clamp_len(const PartialArgs &a, int b, bool flag_it)
 {
     int L = a.seq_lens[b];

@@ -360,7 +360,9 @@ decode_persistent_kernel(PartialArgs a)
     const int pf = nbx_buffer_load_b32(
         make_buffer_rsrc(a.block_table, (uint32_t)min(bt_bytes, (uint64_t)0x7FFFFFF0u)),
         (wv >> 3) * 256 + lane * 4, 0, 0);
-    int Lr[NB], Wr[NB], nsr[NB], incl[NB];
+    // (nsw holds a sequence's split count in its low 16 bits and its window
+    // rows, at most 16, above them: one register per lane block for both)
+    int Lr[NB], Wr[NB], nsw[NB], incl[NB];
     int longest = 1;
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
@@ -387,6 +389,13 @@ decode_persistent_kernel(PartialArgs a)
             longest = max(longest, __shfl_xor(longest, off, 64));
         S = ((longest + NS - 1) / NS + 15) / 16 * 16;
     }
+    // S and N are wave-uniform.  With bounds at D <= 128 they are moved to
+    // scalar registers: that instantiation then spills 16 bytes instead of 36.
+    // Elsewhere the move buys nothing measurable (D <= 128) or makes the
+    // D = 256 instantiations with bounds spill more, so it is not made.
+    constexpr bool kScalarSN = BND && D <= 128;
+    if constexpr (kScalarSN)
+        S = __builtin_amdgcn_readfirstlane(S);
     int carry = 0;
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
@@ -403,11 +412,11 @@ decode_persistent_kernel(PartialArgs a)
             if (lane >= off)
                 x += y;
         }
-        nsr[t] = ns;
+        nsw[t] = ns | (Wr[t] << 16);
         incl[t] = carry + x;
         carry = __shfl(incl[t], 63, 64);
     }
-    const int N = carry;
+    const int N = kScalarSN ? __builtin_amdgcn_readfirstlane(carry) : carry;   // items
     // value of wave-uniform sequence b in a lane table (lane reads of the
     // table registers themselves, valid whatever lanes are active)
     auto lane_val = [&](const int (&arr)[NB], int b) {
@@ -425,7 +434,7 @@ decode_persistent_kernel(PartialArgs a)
         const int per_b = NS * H, pairs = a.batch * per_b;
         for (int pi = wv; pi < pairs; pi += W) {
             const int b = pi / per_b, rem = pi - b * per_b, s = rem / H, gk = rem - s * H;
-            if (s >= lane_val(nsr, b) && lane < M) {
+            if (s >= (lane_val(nsw, b) & 0xFFFF) && lane < M) {
                 const int64_t row =
                     ((int64_t)b * a.q_heads + (int64_t)gk * a.group) * a.q_rows + lane;
                 a.m_part[row * NS + s] = -INFINITY;
@@ -454,11 +463,12 @@ decode_persistent_kernel(PartialArgs a)
         for (int t = 0; t < NB; ++t)
             before += __popcll(__ballot(incl[t] <= k));
         it.b = before;
-        const int excl = lane_val(incl, it.b) - lane_val(nsr, it.b) * H;
+        const int nw = lane_val(nsw, it.b);
+        const int excl = lane_val(incl, it.b) - (nw & 0xFFFF) * H;
         const int r = k - excl;
         it.s = r / H;
         it.gk = r - it.s * H;
-        const int L = lane_val(Lr, it.b), wb = lane_val(Wr, it.b);
+        const int L = lane_val(Lr, it.b), wb = nw >> 16;
         it.j0 = it.s * S;
         it.jend = min(it.j0 + S, seq_keys(L, wb));
         it.nchunk = (it.jend - it.j0 + kChunk - 1) / kChunk;
@@ -466,19 +476,7 @@ decode_persistent_kernel(PartialArgs a)
         it.e_j = min(it.jend, n_j);
         it.row_base = ((int64_t)it.b * a.q_heads + (int64_t)it.gk * a.group) * a.q_rows;
         it.L = L;
-        it.kb = it.vb = 0.0f;
-        if (use_bounds) {                      // the bounds of the pages the item reads
-            const int T = a.page_tokens;
-            for (int pi = it.j0 / T + lane; pi <= (it.jend - 1) / T; pi += 64) {
-                const int page = a.block_table[(int64_t)it.b * a.max_pages + pi];
-                if (page >= 0 && page < a.num_pages) {
-                    it.kb = bound_max(it.kb, a.k_bounds[(int64_t)page * H + it.gk]);
-                    it.vb = bound_max(it.vb, a.v_bounds[(int64_t)page * H + it.gk]);
-                }
-            }
-            it.kb = group_bound_max<64>(it.kb);
-            it.vb = group_bound_max<64>(it.vb);
-        }
+        it.kb = it.vb = 0.0f;                  // raised by the rows the append writes
         return it;
     };
     // Fused append: the new positions L - n_new .. L - 1 that fall in the item
@@ -520,25 +518,50 @@ decode_persistent_kernel(PartialArgs a)
                         raise_bound(a.k_bounds, bi, kn);
                     if (a.v_bounds && lane == 0)
                         raise_bound(a.v_bounds, bi, vm);
-                    it.kb = bound_max(it.kb, kn);
-                    it.vb = bound_max(it.vb, vm);
+                    it.kb = wave_uniform(bound_max(it.kb, kn));
+                    it.vb = wave_uniform(bound_max(it.vb, vm));
                 }
             }
             asm volatile("" ::: "memory");     // keep the tile loads after the stores
         }
     };
+    // the item's Q rows through one descriptor over its M rows: lanes of rows
+    // past M read zeros, and each lane's address is a 32-bit offset
     auto load_q = [&](const Item &it, u32x4 (&qv)[KK]) {
+        const i32x4 rq = make_buffer_rsrc((const uint16_t *)a.q + it.row_base * D,
+                                          (uint32_t)(M * D * 2));
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
-            qv[kk] = j < M ? *(const u32x4 *)((const uint16_t *)a.q + (it.row_base + j) * D +
-                                              kk * 32 + g * 8)
-                           : u32x4{0, 0, 0, 0};
+            qv[kk] = nbx_buffer_load_b128(rq, j * (D * 2) + kk * 64 + g * 16, 0, 0);
     };
     // lane i: page of tile (i & 1) of chunk c0 + i / 2 of the item
     auto item_pages = [&](const Item &it, int c0) {
         const int cq = c0 + (lane >> 1);
         const int ts = it.j0 + cq * kChunk + 16 * (lane & 1);
         return cq < it.nchunk ? tile_page(a, it.b, ts, it.jend, true) : -1;
+    };
+    // Bounds of the pages an item reads (fixed shift), one lane per tile of its
+    // first 32 chunks from its page ids `pg` (item_pages(it, 0)); past those,
+    // the block table is walked.  The loads are issued with the item's first
+    // tiles and reduced once those have landed, so that they wait on nothing
+    // but the page ids.  Lane values; 0 where a lane has no page.
+    float pkb = 0.0f, pvb = 0.0f;
+    auto page_bounds = [&](const Item &it, int pg) {
+        pkb = pvb = 0.0f;
+        if (pg >= 0) {
+            pkb = a.k_bounds[(int64_t)pg * H + it.gk];
+            pvb = a.v_bounds[(int64_t)pg * H + it.gk];
+        }
+        if (it.nchunk > 32) {
+            const int T = a.page_tokens;
+            for (int pi = (it.j0 + 64 * 16) / T + lane; pi <= (it.jend - 1) / T; pi += 64) {
+                const int page = a.block_table[(int64_t)it.b * a.max_pages + pi];
+                if (page >= 0 && page < a.num_pages) {
+                    pkb = bound_max(pkb, a.k_bounds[(int64_t)page * H + it.gk]);
+                    pvb = bound_max(pvb, a.v_bounds[(int64_t)page * H + it.gk]);
+                }
+            }
+        }
     };
 
     const int kst_b = (int)(a.k_stride_token * ESZ), vst_b = (int)(a.v_stride_token * ESZ);
@@ -652,15 +675,19 @@ decode_persistent_kernel(PartialArgs a)
     asm volatile("" ::"v"(pf));                // the prefetch has landed (its value is unused)
     int pg_reg = item_pages(cur, 0), pg_next = -1;
     append_item(cur, pg_reg);
+    if (use_bounds)
+        page_bounds(cur, pg_reg);
     Item nxt = cur;
     bool has_next = false;
+    // the next item and its page ids, one chunk before its loads; its append
+    // and page bounds wait for the switch to it, when the page ids are needed
+    // anyway and no tile load is in flight
     auto prepare_next = [&]() {
         const int kn = wv + (i_item + 1) * W_eff;
         has_next = i_item + 1 < k_per && kn < N;
         if (has_next) {
             nxt = make_item(kn);
             pg_next = item_pages(nxt, 0);
-            append_item(nxt, pg_next);
         }
     };
     int c = 0;
@@ -676,6 +703,11 @@ decode_persistent_kernel(PartialArgs a)
         const int cc = c, cpg0 = pg0, cpg1 = pg1;
         land_v();                              // DS operations of the wave run in order
         land_k();
+        float kb_i = 0.0f, vb_i = 0.0f;        // the item's bounds (its page bounds have landed)
+        if (use_bounds && cc == 0) {
+            kb_i = wave_uniform(group_bound_max<64>(bound_max(pkb, ci.kb)));
+            vb_i = wave_uniform(group_bound_max<64>(bound_max(pvb, ci.vb)));
+        }
         if constexpr (RM) {
             if (cc == 0) {                     // the item's Q (loaded before its K)
 #pragma unroll
@@ -693,6 +725,9 @@ decode_persistent_kernel(PartialArgs a)
             ++i_item;
             c = 0;
             pg_reg = pg_next;
+            append_item(cur, pg_reg);
+            if (use_bounds)
+                page_bounds(cur, pg_reg);
         } else {
             more = false;
         }
@@ -723,8 +758,8 @@ decode_persistent_kernel(PartialArgs a)
         }
         if (use_bounds && cc == 0) {           // the item's Q is still in qb
             int C, gate;
-            bool ok = fixed_shift_consts(ci.L, ci.vb, vs, C, gate);
-            ok = ok && fixed_shift_row(q_row_norm<KK>(qb), ci.kb, fabsf(scale2), C, gate, m_fix);
+            bool ok = fixed_shift_consts(ci.L, vb_i, vs, C, gate);
+            ok = ok && fixed_shift_row(q_row_norm<KK>(qb), kb_i, fabsf(scale2), C, gate, m_fix);
             fixed = __all(ok);
         }
         if (!RM && more) {
