@@ -456,8 +456,21 @@ decode_persistent_kernel(PartialArgs a)
     };
     // fixed-shift softmax: both pools carry per-page bounds
     const bool use_bounds = BND && a.k_bounds != nullptr && a.v_bounds != nullptr;
+    // this lane's window row, j mod q_rows (j < 16), recomputed where it is
+    // needed from a fresh lane id (an asm statement the compiler neither
+    // merges nor keeps live, so that neither j nor the row takes a register
+    // across the main loop)
+    auto window_row = [&]() {
+        int id;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(id));
+        int r = id & 15;
+        while (r >= a.q_rows)
+            r -= a.q_rows;
+        return r;
+    };
     auto make_item = [&](int k) {
         Item it;
+        const int jrow = window_row();
         int before = 0;                        // sequences whose items all precede k
 #pragma unroll
         for (int t = 0; t < NB; ++t)
@@ -472,7 +485,7 @@ decode_persistent_kernel(PartialArgs a)
         it.j0 = it.s * S;
         it.jend = min(it.j0 + S, seq_keys(L, wb));
         it.nchunk = (it.jend - it.j0 + kChunk - 1) / kChunk;
-        const int n_j = j < M ? row_keys(a, L, wb, j % a.q_rows) : 0;
+        const int n_j = j < M ? row_keys(a, L, wb, jrow) : 0;
         it.e_j = min(it.jend, n_j);
         it.row_base = ((int64_t)it.b * a.q_heads + (int64_t)it.gk * a.group) * a.q_rows;
         it.L = L;
