@@ -310,6 +310,34 @@ def test_value_head_dim_matches_torch_sdpa_float64(seed, W, causal, Hq, Hkv, D, 
     assert np.allclose(out, sdpa_reference(p, scale), atol=1e-12, rtol=0)
 
 
+# the storage formats inside attention: a bf16 pool with bf16 Q, and an fp8 pool with
+# per-tensor scales, against torch's float64 attention on torch's own decoding of the
+# same bits (bfloat16 / float8_e4m3fn -> float64, times the scale)
+@pytest.mark.parametrize("seed,kv_dtype,W,causal,Hq,Hkv,D,T,lens,k_scale,v_scale", [
+    (17, "bf16", 1, False, 8, 2, 64, 16, (45, 100), 1.0, 1.0),
+    (18, "bf16", 4, True, 6, 2, 32, 32, (20, 77), 1.0, 1.0),
+    (19, "fp8", 1, False, 4, 1, 32, 16, (31, 64), 0.5, 2.0),
+    (20, "fp8", 3, True, 4, 2, 16, 16, (17, 50), 0.125, 0.25),
+])
+def test_storage_formats_match_torch_sdpa_float64(seed, kv_dtype, W, causal, Hq, Hkv, D, T,
+                                                   lens, k_scale, v_scale):
+    p = contiguous_problem(seed, B=len(lens), Hq=Hq, Hkv=Hkv, W=W, D=D, T=T, lens=lens,
+                           causal=causal)
+    tdt = torch.bfloat16 if kv_dtype == "bf16" else torch.float8_e4m3fn
+    pk = (p["pool_k"] / k_scale).to(tdt)       # the pool's stored codes
+    pv = (p["pool_v"] / v_scale).to(tdt)
+    qb = p["Q"].to(torch.bfloat16)
+    scale = float(np.float32(1 / math.sqrt(D)))
+    out = oracle.attention(qb, "bf16", pk, pv, kv_dtype, p["bt"], p["lens"], scale,
+                           causal=causal, k_scale=k_scale, v_scale=v_scale)
+    # the reference sees torch's decoding of the same codes, laid back out per sequence
+    B, pages = len(lens), p["bt"].shape[1]
+    kd = pk.double().reshape(B, pages, Hkv, T, D).permute(0, 2, 1, 3, 4).reshape(B, Hkv, -1, D)
+    vd = pv.double().reshape(B, pages, Hkv, T, D).permute(0, 2, 1, 3, 4).reshape(B, Hkv, -1, D)
+    ref = sdpa_reference(dict(p, Q=qb.double(), K=kd * k_scale, V=vd * v_scale), scale)
+    assert np.allclose(out, ref, atol=1e-12, rtol=0)
+
+
 # ----------------------------------------------------------------- fixed-shift bounds
 
 def test_fixed_shift_constants_match_the_page_examples():
