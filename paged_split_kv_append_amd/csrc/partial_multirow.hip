@@ -38,7 +38,11 @@ namespace {
 // NTL: the K/V loads are marked non-temporal (one row block per split: no
 // other workgroup reads the same tiles); with several row blocks they stay
 // cacheable, since the row blocks of a split read its tiles from the L2.
-template <int D, int DV, int KVT, bool PVS, int NT, int NK, int NSET, bool NTL>
+// LW (at most 6 x 16 rows, e.g. a 16-row window over 6 query heads): waves
+// 0-5 hold the rows and only compute, wave 6 loads and lands all K pieces and
+// wave 7 all V pieces of each chunk, so that the waves that compute issue no
+// load and no landing (with 8 waves of rows those two waves would hold none).
+template <int D, int DV, int KVT, bool PVS, int NT, int NK, int NSET, bool NTL, bool LW>
 __global__ void __launch_bounds__(512)
 multirow_mfma_kernel(PartialArgs a, int row_blocks)
 {
@@ -58,7 +62,9 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
     constexpr int PMAX = PER_K > PER_V ? PER_K : PER_V;
     static_assert(PER_K <= KK && KK % PER_K == 0 && PER_V <= KV && KV % PER_V == 0,
                   "a wave's pieces lie in one tile");
-    constexpr int R = RW * NT * 16;            // rows per workgroup
+    constexpr int ROWW = LW ? 6 : RW;          // waves holding rows
+    constexpr int R = ROWW * NT * 16;          // rows per workgroup
+    constexpr int PL = KK > KV ? KK : KV;      // LW: pieces per tile of a loader's pool
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF];
 
     const uint32_t id = xcd_contiguous_id(blockIdx.x, gridDim.x);
@@ -75,7 +81,8 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
     const int64_t row_base = ((int64_t)b * a.q_heads + (int64_t)gk * a.group) * a.q_rows;
     const bool lead = threadIdx.x == 0;
     // a wave whose row tiles are all past the last row loads its share only
-    const bool has_rows = row_lo + w * NT * 16 < row_hi;
+    const bool has_rows = w < ROWW && row_lo + w * NT * 16 < row_hi;
+    const bool loader = LW && w >= ROWW;       // LW: wave 6 loads K, wave 7 V
 
     const int S = device_split_size(a);
     const int L = clamp_len(a, b, lead && s == 0 && rb == 0);
@@ -98,58 +105,6 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
     const int jend = min(j0 + S, n_max);
     const int nchunk = jend > j0 ? (jend - j0 + CH - 1) / CH : 0;
 
-    u32x4 qb[NT][KK];
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-        const int m = row_lo + (w * NT + n) * 16 + j;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-            qb[n][kk] = m < row_hi ? *(const u32x4 *)((const uint16_t *)a.q + (row_base + m) * D +
-                                                      kk * 32 + g * 8)
-                                   : u32x4{0, 0, 0, 0};
-    }
-    const float scale2 = a.scale * a.k_scale * kLog2e;
-    float m_run[NT], m_top[NT], l_run[NT];     // shift (lazy), maximum, sum of each row
-    f32x4 o[NT][DT];
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-        m_run[n] = -INFINITY;
-        m_top[n] = -INFINITY;
-        l_run[n] = 0.0f;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-            o[n][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-    // fixed-shift softmax where both pools carry bounds: per row tile, a shift
-    // per row and one decision for the tile's 16 rows
-    bool fixed[NT];
-    float m_fix[NT];
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-        fixed[n] = false;
-        m_fix[n] = 0.0f;
-    }
-    if (a.k_bounds != nullptr && a.v_bounds != nullptr && nchunk > 0) {
-        float kb = 0.0f, vb = 0.0f;
-        const int T = a.page_tokens;
-        for (int pi = j0 / T + lane; pi <= (jend - 1) / T; pi += 64) {
-            const int page = a.block_table[(int64_t)b * a.max_pages + pi];
-            if (page >= 0 && page < a.num_pages) {
-                kb = bound_max(kb, a.k_bounds[(int64_t)page * a.kv_heads + gk]);
-                vb = bound_max(vb, a.v_bounds[(int64_t)page * a.kv_heads + gk]);
-            }
-        }
-        kb = group_bound_max<64>(kb);
-        vb = group_bound_max<64>(vb);
-        int C, gate;
-        if (fixed_shift_consts(L, vb, a.v_scale, C, gate)) {
-#pragma unroll
-            for (int n = 0; n < NT; ++n)
-                fixed[n] = __all(fixed_shift_row(q_row_norm<KK>(qb[n]), kb, fabsf(scale2), C, gate,
-                                                 m_fix[n]));
-        }
-    }
-
     const int64_t k_head = (int64_t)gk * a.k_stride_head;
     const int64_t v_head = (int64_t)gk * a.v_stride_head;
     const int kst_b = (int)(a.k_stride_token * ESZ), vst_b = (int)(a.v_stride_token * ESZ);
@@ -166,7 +121,7 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
     // (tile-major: K 32-column groups kk, V 32-column pairs of 16-column
     // slices) wave w takes (w & 3) * per ... (w & 3) * per + per - 1, all in
     // tile t_w of every chunk.
-    const bool is_k = w < 4;
+    const bool is_k = LW ? w != 7 : w < 4;    // (LW: the row waves' role only sets kvalid)
     const int per = is_k ? PER_K : PER_V, pieces = is_k ? KK : KV;
     const int t_w = ((w & 3) * per) / pieces, pbase = ((w & 3) * per) % pieces;
     const uint8_t *role_base = is_k ? (const uint8_t *)a.k_data + k_head * ESZ
@@ -246,6 +201,127 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
                 *(u32x4 *)(dst + x * 1024) = widen8_e4m3(rg.r8[x]);
         }
     };
+    // LW: a loader's pieces of all tiles of chunk c, one descriptor per tile
+    struct RegsL {
+        u32x4 r16[BF ? TL * PL : 1];
+        u32x2 r8[BF ? 1 : TL * PL];
+    };
+    const int lw_pieces = is_k ? KK : KV;
+    const int lw_lane = is_k ? k_lane : v_lane;
+    auto issue_all = [&](int c, RegsL &rg) {
+        const int q = (c / BATCH) & 1;
+#pragma unroll
+        for (int t = 0; t < TL; ++t) {
+            const int li = TL * (c % BATCH) + t;
+            const uint32_t lo = __builtin_amdgcn_readlane(q ? off_lo1 : off_lo0, li);
+            const uint32_t hi = __builtin_amdgcn_readlane(q ? off_hi1 : off_hi0, li);
+            const uint32_t nb = __builtin_amdgcn_readlane(q ? nbytes1 : nbytes0, li);
+            const i32x4 rs = make_buffer_rsrc(role_base + (((uint64_t)hi << 32) | lo), nb);
+#pragma unroll
+            for (int x = 0; x < PL; ++x) {
+                if (x >= lw_pieces)
+                    break;
+                if constexpr (BF)
+                    rg.r16[t * PL + x] = nbx_buffer_load_b128(rs, lw_lane + x * 32 * ESZ, 0,
+                                                              NTL ? kStreamAux : 0);
+                else
+                    rg.r8[t * PL + x] = nbx_buffer_load_b64(rs, lw_lane + x * 32 * ESZ, 0,
+                                                            NTL ? kStreamAux : 0);
+            }
+        }
+    };
+    auto land_all = [&](uint8_t *buf, const RegsL &rg) {
+#pragma unroll
+        for (int t = 0; t < TL; ++t) {
+            uint8_t *dst = is_k ? buf + t * KK * 1024 + k_st
+                                : buf + KBYTES + t * DT * 512 + lane * 16;
+#pragma unroll
+            for (int x = 0; x < PL; ++x) {
+                if (x >= lw_pieces)
+                    break;
+                if constexpr (BF)
+                    *(u32x4 *)(dst + x * 1024) = rg.r16[t * PL + x];
+                else
+                    *(u32x4 *)(dst + x * 1024) = widen8_e4m3(rg.r8[t * PL + x]);
+            }
+        }
+    };
+    // LW: the loaders run their own loop and leave; the row state below is
+    // never live in them.  Iteration c: barrier (every wave is done with chunk
+    // c - 1), land chunk c + 1 into buffer (c + 1) & 1, issue chunk c + 2 —
+    // one barrier per chunk, as the row waves.
+    if constexpr (LW) {
+        if (loader) {
+            RegsL lr;
+            if (nchunk > 0) {
+                refresh(0);
+                issue_all(0, lr);
+                land_all(smem, lr);
+                issue_all(1, lr);
+                for (int c = 0; c < nchunk; ++c) {
+                    __syncthreads();
+                    land_all(smem + ((c + 1) & 1) * BUF, lr);
+                    if ((c + 2) % BATCH == 0)
+                        refresh(c + 2);
+                    issue_all(c + 2, lr);
+                }
+            }
+            return;
+        }
+    }
+
+    u32x4 qb[NT][KK];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        const int m = row_lo + (w * NT + n) * 16 + j;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+            qb[n][kk] = m < row_hi ? *(const u32x4 *)((const uint16_t *)a.q + (row_base + m) * D +
+                                                      kk * 32 + g * 8)
+                                   : u32x4{0, 0, 0, 0};
+    }
+    const float scale2 = a.scale * a.k_scale * kLog2e;
+    float m_run[NT], m_top[NT], l_run[NT];     // shift (lazy), maximum, sum of each row
+    f32x4 o[NT][DT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        m_run[n] = -INFINITY;
+        m_top[n] = -INFINITY;
+        l_run[n] = 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+            o[n][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    // fixed-shift softmax where both pools carry bounds: per row tile, a shift
+    // per row and one decision for the tile's 16 rows
+    bool fixed[NT];
+    float m_fix[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        fixed[n] = false;
+        m_fix[n] = 0.0f;
+    }
+    if (a.k_bounds != nullptr && a.v_bounds != nullptr && nchunk > 0) {
+        float kb = 0.0f, vb = 0.0f;
+        const int T = a.page_tokens;
+        for (int pi = j0 / T + lane; pi <= (jend - 1) / T; pi += 64) {
+            const int page = a.block_table[(int64_t)b * a.max_pages + pi];
+            if (page >= 0 && page < a.num_pages) {
+                kb = bound_max(kb, a.k_bounds[(int64_t)page * a.kv_heads + gk]);
+                vb = bound_max(vb, a.v_bounds[(int64_t)page * a.kv_heads + gk]);
+            }
+        }
+        kb = group_bound_max<64>(kb);
+        vb = group_bound_max<64>(vb);
+        int C, gate;
+        if (fixed_shift_consts(L, vb, a.v_scale, C, gate)) {
+#pragma unroll
+            for (int n = 0; n < NT; ++n)
+                fixed[n] = __all(fixed_shift_row(q_row_norm<KK>(qb[n]), kb, fabsf(scale2), C, gate,
+                                                 m_fix[n]));
+        }
+    }
+
     auto compute = [&](int c, int boff) {
         const int p0 = j0 + c * CH;
         bool ok[TL];
@@ -338,6 +414,20 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
     // descriptors are empty, so they read zeros and touch no memory): with no
     // branch around them the waits for each register set stay exact and the
     // chunks behind it stay in flight.
+    if constexpr (LW) {
+        // Iteration c: barrier, then the row waves compute chunk c (the
+        // loaders, which returned above, land chunk c + 1 meanwhile).
+        if (nchunk > 0) {
+            refresh(0);
+            for (int c = 0; c < nchunk; ++c) {
+                __syncthreads();
+                if (has_rows)
+                    compute(c, (c & 1) * BUF);
+                if ((c + 2) % BATCH == 0)
+                    refresh(c + 2);
+            }
+        }
+    } else {
     Regs rset[NSET];
     auto step = [&](int c, Regs &land_regs) {
         __syncthreads();
@@ -360,6 +450,7 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
             for (int r = 0; r < NSET; ++r)     // lands c + r + 1, reissues c + r + 1 + NSET there
                 step(c + r, rset[r]);
         }
+    }
     }
 
     const float vs = a.v_scale;
@@ -402,16 +493,19 @@ hipError_t launch_mr(const PartialArgs &a, hipStream_t stream)
         return hipErrorInvalidConfiguration;
     if constexpr (D <= 128) {                 // two row tiles per wave only below D = 256
         if (nt == 2) {                         // (more than 128 rows: several row blocks)
-            hipLaunchKernelGGL((multirow_mfma_kernel<D, DV, KVT, PVS, 2, kMrNK, kMrNSet, false>),
+            hipLaunchKernelGGL((multirow_mfma_kernel<D, DV, KVT, PVS, 2, kMrNK, kMrNSet, false, false>),
                                dim3((unsigned)blocks), dim3(512), 0, stream, a, row_blocks);
             return hipGetLastError();
         }
     }
-    if (row_blocks == 1)
-        hipLaunchKernelGGL((multirow_mfma_kernel<D, DV, KVT, PVS, 1, kMrNK, kMrNSet, true>),
+    if (M <= 96)                               // rows fit 6 waves: two dedicated loaders
+        hipLaunchKernelGGL((multirow_mfma_kernel<D, DV, KVT, PVS, 1, kMrNK, kMrNSet, true, true>),
+                           dim3((unsigned)blocks), dim3(512), 0, stream, a, row_blocks);
+    else if (row_blocks == 1)
+        hipLaunchKernelGGL((multirow_mfma_kernel<D, DV, KVT, PVS, 1, kMrNK, kMrNSet, true, false>),
                            dim3((unsigned)blocks), dim3(512), 0, stream, a, row_blocks);
     else
-        hipLaunchKernelGGL((multirow_mfma_kernel<D, DV, KVT, PVS, 1, kMrNK, kMrNSet, false>),
+        hipLaunchKernelGGL((multirow_mfma_kernel<D, DV, KVT, PVS, 1, kMrNK, kMrNSet, false, false>),
                            dim3((unsigned)blocks), dim3(512), 0, stream, a, row_blocks);
     return hipGetLastError();
 }
