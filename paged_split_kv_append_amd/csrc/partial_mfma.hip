@@ -45,11 +45,14 @@
 //  - decode_mfma_kernel: the same rows for larger batches.  PG waves per
 //    (split, sequence x KV head) take interleaved chunks of the split, each
 //    with its own (m, l, O), combined in a fixed order at the end.
-// In both, K rows go from HBM straight into MFMA operand registers; V rows
-// are loaded into registers and written to the wave's LDS tile once they land
-// (fp8 codes widened on the way).  The wave's next chunk is loaded while the
-// current one is computed.  The persistent kernel also takes the fixed-shift
-// softmax (partial_common.h) when both pools carry per-page bounds.
+// In decode_mfma_kernel, and in the persistent kernel for fp8 pools, K rows go
+// from HBM straight into MFMA operand registers (16 rows x 64 bytes per load)
+// and V rows are written to the wave's LDS tile once they land (fp8 codes
+// widened on the way).  The persistent kernel loads bf16 K and V tiles as
+// whole rows (64 consecutive 16-byte units per load, RowTile) into LDS and
+// reads K back in the operand layout.  The wave's next chunk is loaded while
+// the current one is computed.  The persistent kernel also takes the
+// fixed-shift softmax (partial_common.h) when both pools carry per-page bounds.
 #include <atomic>
 
 #include "partial_common.h"
@@ -323,9 +326,9 @@ constexpr int kPersistMaxBatch = 256;      // sequences covered by the lane-regi
 // m = -inf and l = 0; their o is not written.  BND: a pool carries bounds
 // (raised by the fused append; with both, the fixed-shift softmax), a
 // separate instantiation so that the plain kernel keeps its registers; at
-// D = 128 it is held to 2 waves per SIMD like the plain one (it fits 256
-// registers without spilling; left to itself the compiler takes one more
-// AGPR block and halves the resident waves).
+// D = 128 it is held to 2 waves per SIMD like the plain one (256 registers,
+// 12 bytes spilled outside the streaming path; left to itself the compiler
+// takes one more AGPR block and halves the resident waves).
 template <int D, int DV, int KVT, bool PVS, int NB, bool FA, bool BND>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(((BND || KVT == NBX_BF16) && D == 128) ? 2 : 1)))
 decode_persistent_kernel(PartialArgs a)
