@@ -347,6 +347,17 @@ MULTIROW = [
                               lens=("uniform", 40, 700), append=False)),
     ("d64_bf16_288rows", dict(batch=2, head_dim=64, q_rows=72, causal=True,
                               lens=("uniform", 72, 600), append=False)),
+    # at most 96 rows: two loader waves; 96 rows exactly at D = 256, a ragged
+    # last row tile (76 rows), the 192 / 128 pair (K and V pieces per tile
+    # differ), and 100 rows just past the loader form
+    ("d256_bf16_96rows", dict(batch=2, head_dim=256, q_rows=24, causal=True,
+                              lens=("uniform", 24, 700), append=False)),
+    ("d128_fp8_76rows", dict(batch=3, kv_dtype="fp8", q_rows=19, causal=True,
+                             lens=("uniform", 19, 800), append=False)),
+    ("d192_v128_bf16_64rows", dict(batch=2, head_dim=192, v_head_dim=128, q_rows=16,
+                                   causal=True, lens=("uniform", 16, 600), append=False)),
+    ("d128_bf16_100rows", dict(batch=2, q_rows=25, causal=True, lens=("uniform", 25, 600),
+                               append=False)),
 ]
 
 
