@@ -208,62 +208,66 @@ multirow_mfma_kernel(PartialArgs a, int row_blocks)
     };
     const int lw_pieces = is_k ? KK : KV;
     const int lw_lane = is_k ? k_lane : v_lane;
-    auto issue_all = [&](int c, RegsL &rg) {
-        const int q = (c / BATCH) & 1;
+    // tile t of chunk c: its pieces into registers / from registers into LDS
+    auto issue_tile = [&](int c, RegsL &rg, int t) {
+        const int q = (c / BATCH) & 1, li = TL * (c % BATCH) + t;
+        const uint32_t lo = __builtin_amdgcn_readlane(q ? off_lo1 : off_lo0, li);
+        const uint32_t hi = __builtin_amdgcn_readlane(q ? off_hi1 : off_hi0, li);
+        const uint32_t nb = __builtin_amdgcn_readlane(q ? nbytes1 : nbytes0, li);
+        const i32x4 rs = make_buffer_rsrc(role_base + (((uint64_t)hi << 32) | lo), nb);
 #pragma unroll
-        for (int t = 0; t < TL; ++t) {
-            const int li = TL * (c % BATCH) + t;
-            const uint32_t lo = __builtin_amdgcn_readlane(q ? off_lo1 : off_lo0, li);
-            const uint32_t hi = __builtin_amdgcn_readlane(q ? off_hi1 : off_hi0, li);
-            const uint32_t nb = __builtin_amdgcn_readlane(q ? nbytes1 : nbytes0, li);
-            const i32x4 rs = make_buffer_rsrc(role_base + (((uint64_t)hi << 32) | lo), nb);
-#pragma unroll
-            for (int x = 0; x < PL; ++x) {
-                if (x >= lw_pieces)
-                    break;
-                if constexpr (BF)
-                    rg.r16[t * PL + x] = nbx_buffer_load_b128(rs, lw_lane + x * 32 * ESZ, 0,
-                                                              NTL ? kStreamAux : 0);
-                else
-                    rg.r8[t * PL + x] = nbx_buffer_load_b64(rs, lw_lane + x * 32 * ESZ, 0,
-                                                            NTL ? kStreamAux : 0);
-            }
+        for (int x = 0; x < PL; ++x) {
+            if (x >= lw_pieces)
+                break;
+            if constexpr (BF)
+                rg.r16[t * PL + x] = nbx_buffer_load_b128(rs, lw_lane + x * 32 * ESZ, 0,
+                                                          NTL ? kStreamAux : 0);
+            else
+                rg.r8[t * PL + x] = nbx_buffer_load_b64(rs, lw_lane + x * 32 * ESZ, 0,
+                                                        NTL ? kStreamAux : 0);
         }
     };
-    auto land_all = [&](uint8_t *buf, const RegsL &rg) {
+    auto land_tile = [&](uint8_t *buf, const RegsL &rg, int t) {
+        uint8_t *dst = is_k ? buf + t * KK * 1024 + k_st : buf + KBYTES + t * DT * 512 + lane * 16;
 #pragma unroll
-        for (int t = 0; t < TL; ++t) {
-            uint8_t *dst = is_k ? buf + t * KK * 1024 + k_st
-                                : buf + KBYTES + t * DT * 512 + lane * 16;
-#pragma unroll
-            for (int x = 0; x < PL; ++x) {
-                if (x >= lw_pieces)
-                    break;
-                if constexpr (BF)
-                    *(u32x4 *)(dst + x * 1024) = rg.r16[t * PL + x];
-                else
-                    *(u32x4 *)(dst + x * 1024) = widen8_e4m3(rg.r8[t * PL + x]);
-            }
+        for (int x = 0; x < PL; ++x) {
+            if (x >= lw_pieces)
+                break;
+            if constexpr (BF)
+                *(u32x4 *)(dst + x * 1024) = rg.r16[t * PL + x];
+            else
+                *(u32x4 *)(dst + x * 1024) = widen8_e4m3(rg.r8[t * PL + x]);
         }
     };
     // LW: the loaders run their own loop and leave; the row state below is
     // never live in them.  Iteration c: barrier (every wave is done with chunk
-    // c - 1), land chunk c + 1 into buffer (c + 1) & 1, issue chunk c + 2 —
-    // one barrier per chunk, as the row waves.
+    // c - 1), then for each tile land it for chunk c + 1 into buffer
+    // (c + 1) & 1 and reload its registers with chunk c + 2 — one barrier per
+    // chunk, as the row waves.
     if constexpr (LW) {
         if (loader) {
             RegsL lr;
             if (nchunk > 0) {
                 refresh(0);
-                issue_all(0, lr);
-                land_all(smem, lr);
-                issue_all(1, lr);
+#pragma unroll
+                for (int t = 0; t < TL; ++t)
+                    issue_tile(0, lr, t);
+#pragma unroll
+                for (int t = 0; t < TL; ++t) {
+                    land_tile(smem, lr, t);
+                    issue_tile(1, lr, t);
+                }
                 for (int c = 0; c < nchunk; ++c) {
                     __syncthreads();
-                    land_all(smem + ((c + 1) & 1) * BUF, lr);
                     if ((c + 2) % BATCH == 0)
                         refresh(c + 2);
-                    issue_all(c + 2, lr);
+                    // (the first tiles of chunk c + 2 are in flight while the
+                    // later ones of c + 1 land)
+#pragma unroll
+                    for (int t = 0; t < TL; ++t) {
+                        land_tile(smem + ((c + 1) & 1) * BUF, lr, t);
+                        issue_tile(c + 2, lr, t);
+                    }
                 }
             }
             return;
